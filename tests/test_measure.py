@@ -1,0 +1,51 @@
+"""Pins for the report's counting and roofline arithmetic against numbers the
+pages print (fixtures under tests/golden, each with its citation)."""
+import pytest
+
+from conftest import read_golden
+from precision_gemm_amd import measure
+import workloads
+
+
+def test_page_counts_for_4092():
+    g = read_golden("page_counts.txt")
+    flops = measure.gemm_flops(4092, 4092, 4092)
+    assert round(flops / 1e9) == g["gemm_4092_gflop"]
+    assert flops == workloads.HEADLINE.flops()
+    assert round(measure.naive_kernel_read_bytes(4092, 4092, 4092) / 1e9) == g["naive_read_gb"]
+    assert measure.block_tile_intensity(128, 128) == g["block_ai_128"]
+    assert measure.block_tile_intensity(32, 32) == g["block_ai_32"]
+    tm = 8
+    assert (1 + tm) / tm == g["loads_per_fma_tm8"]
+
+
+def test_roofline_reproduces_printed_lab_output():
+    g = read_golden("roofline_p3.txt")
+    peak, bw = g["peak_tflops"] * 1e12, g["bw_tbs"] * 1e12
+    soft = measure.roofline(g["softmax_ai"] * 1000.0, 1000.0, peak, bw)
+    assert f"{soft.ridge:.1f}" == f"{g['ridge']:.1f}"
+    assert soft.bound == "memory-bound"
+    assert f"{soft.attainable / 1e12:.1f}" == f"{g['softmax_attainable_tflops']:.1f}"
+    assert f"{soft.frac_of_peak * 100:.1f}" == f"{g['softmax_pct']:.1f}"
+    gemm = measure.roofline(g["gemm_ai"] * 1000.0, 1000.0, peak, bw)
+    assert gemm.bound == "compute-bound"
+    assert f"{gemm.attainable / 1e12:.1f}" == f"{g['gemm_attainable_tflops']:.1f}"
+    assert f"{gemm.frac_of_peak * 100:.1f}" == f"{g['gemm_pct']:.1f}"
+    # the printed GEMM intensity is 2N^3 flops over three N x N matrices of 2-byte elements
+    n = 4096
+    assert f"{2 * n**3 / (3 * n * n * 2):.1f}" == f"{g['gemm_ai']:.1f}"
+
+
+def test_mi355x_workload_rooflines():
+    """The five workloads against MI355X FP32-MFMA peak and HBM bandwidth."""
+    by = workloads.BY_NAME
+    roofs = {n: measure.roofline(w.flops(), w.algorithmic_bytes(),
+                                 measure.MI355X_FP32_MFMA_PEAK, measure.MI355X_HBM_BW)
+             for n, w in by.items()}
+    assert roofs["sgemm_4092"].bound == "compute-bound"
+    assert roofs["sgemm_4092"].intensity == pytest.approx(511.5, abs=0.05)
+    assert roofs["skinny_16384x64x4096_nt"].intensity == pytest.approx(30.9, abs=0.05)
+    assert roofs["sgemm_4092"].ridge == pytest.approx(19.66, abs=0.01)
+    # 70 % of FP32-MFMA peak at 4092^3 is 110.1 TFLOP/s, i.e. at most 1.2445 ms
+    t = by["sgemm_4092"].flops() / (0.7 * measure.MI355X_FP32_MFMA_PEAK)
+    assert t == pytest.approx(1.2445e-3, rel=1e-4)
