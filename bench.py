@@ -1,0 +1,218 @@
+#!/usr/bin/env python3
+"""Benchmark: SGEMM GFLOP/s and fraction of MI355X FP32-MFMA peak.
+
+One step is one call of the library's ``sgemm`` on the workload (by default
+M = N = K = 4092, alpha = 1, beta = 0.5, the size "From 1% to 94% of cuBLAS,
+one kernel at a time" benchmarks) with its operands already resident in HBM.
+W untimed warm-up steps run first, then exactly K steps are timed between two
+device synchronisations with HIP events recorded on the stream the kernels
+run on (torch's current stream, which is the one passed to the library).
+Each timed step is also bracketed by its own event pair, giving the average
+duration of one kernel launch for the roofline figure.
+
+Prints one JSON line. ``value`` is GFLOP/s (2*M*N*K per GEMM over the timed
+wall time). ``roofline`` reports the same kernel against the FP32-MFMA peak;
+``traffic`` (HBM bytes per launch) is read from the committed rocprofv3
+counter summary if that summary was taken on the current kernel source, else
+null. ``cpu_baseline`` times the CPU oracle on a bounded sample of the same
+workload (a band of output rows) on this host's cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "SGEMM GFLOP/s and % of FP32-MFMA peak at M=N=K=4092 (1 MI355X)"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    with open(os.path.join(ROOT, "precision_gemm_amd", "csrc", "sgemm.hip"), "rb") as f:
+        h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload: str):
+    """HBM bytes per launch from the committed counter summary, if current."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            data = json.load(f)
+    except (OSError, ValueError):
+        return None
+    entry = data.get(workload)
+    if not entry or entry.get("kernel_sha") != kernel_source_hash():
+        return None
+    return entry.get("bytes_per_launch")
+
+
+def cpu_baseline(w, A, B, C, got_c, target_s: float):
+    """Time the CPU oracle on a band of output rows (about target_s seconds)."""
+    import numpy as np
+    import oracle
+
+    threads = oracle.default_threads()
+    per_row_flops = 2.0 * w.N * w.K * w.batch
+
+    def run(rows):
+        t0 = time.perf_counter()
+        ref, S = oracle.sgemm_rows(w.trans_a, w.trans_b, w.M, w.N, w.K, w.alpha, A, w.LDA,
+                                   B, w.LDB, w.beta, C, w.LDC, batch=w.batch,
+                                   stride_a=w.SA, stride_b=w.SB, stride_c=w.SC,
+                                   rows=(0, rows), threads=threads)
+        return time.perf_counter() - t0, ref, S
+
+    probe_rows = min(w.M, max(threads, 16))
+    t_probe, _, _ = run(probe_rows)
+    rows = int(min(w.M, max(probe_rows, probe_rows * target_s / max(t_probe, 1e-6))))
+    rows = max(1, rows - rows % threads) if rows > threads else rows
+    t, ref, S = run(rows)
+    gflops = rows * per_row_flops / t / 1e9
+    # the sampled rows double as a parity check of the first timed launch
+    g = np.stack([np.lib.stride_tricks.as_strided(
+        got_c[b * w.SC:], (rows, w.N), (w.LDC * 4, 4)) for b in range(w.batch)])
+    cin = np.stack([np.lib.stride_tricks.as_strided(
+        C[b * w.SC:], (rows, w.N), (w.LDC * 4, 4)) for b in range(w.batch)])
+    rep = oracle.bound_check(g, ref, S, cin, w.alpha, w.beta, w.K)
+    return {
+        "value": round(gflops, 3),
+        "unit": "GFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": (f"rows 0..{rows - 1} of the {w.M}x{w.N}x{w.K} product "
+                   f"({rows}x{w.N}x{w.K} multiply-adds, fp64 accumulation), "
+                   f"{t:.2f} s on {threads} threads"),
+        "seconds": round(t, 3),
+        "sample_parity": {"ok": rep.ok, "max_norm_err": rep.max_norm_err,
+                          "limit": oracle.TOL_PER_K},
+    }
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="sgemm_4092", help="workload name (workloads.py)")
+    ap.add_argument("--variant", type=int, default=-1, help="force a kernel variant (-1 auto)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="approximate CPU time for the oracle baseline sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true",
+                    help="skip the oracle leg (profiling runs)")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (--gpus {args.gpus} requested); "
+              "sharding across GPUs is described in the design notes, not run.",
+              file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import precision_gemm_amd as pg
+    from precision_gemm_amd import measure
+    import workloads
+
+    w = workloads.BY_NAME[args.config]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    props = torch.cuda.get_device_properties(dev)
+    A, B, C = workloads.make_inputs(w)
+    dA, dB, dC = (torch.from_numpy(x).to(dev) for x in (A, B, C))
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        pg.sgemm_strided_batched_variant(w.trans_a, w.trans_b, w.M, w.N, w.K, w.alpha, dA,
+                                         w.LDA, dB, w.LDB, w.beta, dC, w.LDC, w.batch, w.SA,
+                                         w.SB, w.SC, args.variant, stream=stream.cuda_stream)
+
+    # First launch on pristine inputs: its output is what the oracle sample checks.
+    step()
+    torch.cuda.synchronize(dev)
+    first_out = dC.cpu().numpy() if not args.no_cpu_baseline else None
+
+    for _ in range(max(0, args.warmup - 1)):
+        step()
+    torch.cuda.synchronize(dev)
+
+    K = args.steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(K)]
+    region0, region1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize(dev)
+    region0.record(stream)
+    for s in range(K):
+        ev[s][0].record(stream)
+        step()
+        ev[s][1].record(stream)
+    region1.record(stream)
+    torch.cuda.synchronize(dev)
+
+    total_ms = region0.elapsed_time(region1)
+    per_launch_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    ms_per_step = total_ms / K
+    flops = w.flops()
+    value = flops / (ms_per_step * 1e-3) / 1e9
+
+    vec4_ok = True  # torch allocations are 256-B aligned; the workloads use ld % 4 == 0
+    variant = args.variant if args.variant >= 0 else pg.sgemm_select_variant(
+        w.trans_a, w.trans_b, w.M, w.N, w.K, w.batch, vec4_ok, props.multi_processor_count)
+
+    achieved = flops / (per_launch_ms * 1e-3) / 1e12
+    peak = measure.MI355X_FP32_MFMA_PEAK / 1e12
+    roof = measure.roofline(flops, w.algorithmic_bytes(), measure.MI355X_FP32_MFMA_PEAK,
+                            measure.MI355X_HBM_BW)
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name,
+            "M": w.M, "N": w.N, "K": w.K, "batch": w.batch,
+            "transA": w.trans_a, "transB": w.trans_b,
+            "alpha": w.alpha, "beta": w.beta,
+            "inputs": f"{'U(-1,1)' if w.dist == 'uniform' else 'N(0,1)'} fp32, seed {w.seed}",
+            "variant": pg.VARIANT_NAMES.get(variant, str(variant)),
+            "device": props.name,
+            "cus": props.multi_processor_count,
+        },
+        "pct_of_fp32_mfma_peak": round(100.0 * value * 1e9 / measure.MI355X_FP32_MFMA_PEAK, 2),
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(achieved, 3),
+            "peak": peak,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / peak, 4),
+            "traffic": load_traffic(w.name),
+            "arithmetic_intensity": round(roof.intensity, 2),
+            "hbm_gbs_at_achieved": round(w.algorithmic_bytes() / (per_launch_ms * 1e-3) / 1e9, 1),
+            "kernel_ms": round(per_launch_ms, 5),
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, A, B, C, first_out, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,126 @@
+/*
+ * libsgemm — single-precision GEMM for AMD Instinct MI355X (gfx950).
+ *
+ * Computes C = alpha * op(A) @ op(B) + beta * C in fp32, the SGEMM of
+ * "From 1% to 94% of cuBLAS, one kernel at a time" (the paragraph defining
+ * SGEMM: A is M x K, B is K x N, C is M x N, each output a length-K dot
+ * product, row-major storage), with transposed operands expressed as swapped
+ * strides as in "Triton Optimization Reference (cuTile -> Triton)", section 2
+ * (transpose in pointer arithmetic), and a strided-batched form whose batch
+ * index is the second grid axis as in section 3 (grid layout) of that page.
+ *
+ * Storage (row-major throughout, element strides):
+ *   op(A)[i,k] = transA ? A[k*lda + i] : A[i*lda + k]   (A stored K x M or M x K)
+ *   op(B)[k,j] = transB ? B[j*ldb + k] : B[k*ldb + j]   (B stored N x K or K x N)
+ *   C[i,j]     = C[i*ldc + j]
+ *   batch item b uses A + b*strideA, B + b*strideB, C + b*strideC.
+ *
+ * Ownership: A, B and C are DEVICE pointers owned by the caller; the library
+ * keeps no reference after the call returns and allocates no memory.
+ *
+ * Execution: every call is asynchronous on `stream` (a hipStream_t; NULL is
+ * the default stream) and never synchronises the host. Results are
+ * deterministic: the same call on the same inputs gives the same bits.
+ * Calls are thread-safe.
+ *
+ * Special cases:
+ *   - M == 0, N == 0 or batch == 0: nothing is launched.
+ *   - alpha == 0 or K == 0: C = beta * C; A and B are not read
+ *     (and nothing is launched if beta == 1).
+ *   - beta == 0: C is not read, so NaN or Inf already in C never propagates.
+ *
+ * Accuracy: products and sums are full fp32 (FP32 MFMA, no reduced-precision
+ * inputs); each element is within 2e-6 * max(K,1) * (|alpha| * sum_k
+ * |op(A)[i,k] op(B)[k,j]| + |beta| |C[i,j]|) of the exact result.
+ *
+ * Return value (int status):
+ *     0  success (the work is queued on the stream);
+ *    <0  -(position of the first invalid argument), counted from 1 in the
+ *        sgemm_strided_batched argument list: transA -1, transB -2, M -3,
+ *        N -4, K -5, A -7, lda -8, B -9, ldb -10, C -12, ldc -13,
+ *        batch -14, strideA -15, strideB -16, strideC -17 (negative).
+ *        A leading dimension must be at least the stored row length
+ *        (lda >= max(1, transA ? M : K), ldb >= max(1, transB ? K : N),
+ *        ldc >= max(1, N)) and below 2^21 elements, which keeps every
+ *        in-tile byte offset within 31 bits. A NULL pointer is an error only
+ *        where it would be dereferenced. Nothing is launched on error.
+ *    >0  a hipError_t raised when querying the device or launching.
+ * sgemm_status_string() turns any status into a message.
+ *
+ * Alignment: none is required. When A, B and C are 16-byte aligned and
+ * lda, ldb, ldc (and the batch strides) are multiples of 4, the kernels move
+ * four floats per load; otherwise a one-float-per-load variant runs.
+ */
+#ifndef PRECISION_GEMM_AMD_SGEMM_H
+#define PRECISION_GEMM_AMD_SGEMM_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef void *sgemm_stream_t; /* hipStream_t; NULL = the default stream */
+
+/* C = alpha * op(A) @ op(B) + beta * C for one matrix triple (batch = 1). */
+int sgemm(int transA, int transB, int M, int N, int K,
+          float alpha, const float *A, int lda,
+                       const float *B, int ldb,
+          float beta,        float *C, int ldc,
+          sgemm_stream_t stream);
+
+/* The same for `batch` independent triples at element strides strideA,
+ * strideB, strideC. strideA or strideB may be 0 (one operand shared by every
+ * item); C items must not overlap each other, A or B. */
+int sgemm_strided_batched(int transA, int transB, int M, int N, int K,
+                          float alpha, const float *A, int lda,
+                                       const float *B, int ldb,
+                          float beta,        float *C, int ldc,
+                          int batch, long long strideA, long long strideB,
+                          long long strideC,
+                          sgemm_stream_t stream);
+
+/* Message for a status returned by any entry point (static storage). */
+const char *sgemm_status_string(int status);
+
+/*
+ * Kernel variants the dispatcher chooses among (see sgemm_select_variant).
+ * The tile of C one workgroup owns, its waves, and the load width.
+ */
+enum sgemm_variant {
+    SGEMM_VARIANT_AUTO = -1,
+    SGEMM_VARIANT_L256x128 = 0, /* 256 x 128 tile, 4 waves, 4-float loads */
+    SGEMM_VARIANT_M128x128 = 1, /* 128 x 128 tile, 4 waves, 4-float loads */
+    SGEMM_VARIANT_S64x64 = 2,   /*  64 x  64 tile, 4 waves, 4-float loads */
+    SGEMM_VARIANT_S64x64_V1 = 3,/*  64 x  64 tile, 4 waves, 1-float loads (any alignment) */
+    SGEMM_VARIANT_COUNT = 4
+};
+
+/*
+ * Host-side dispatch decision, exposed for tests and tuning (no device call):
+ * the variant sgemm_strided_batched would launch for this shape, given
+ * whether the 4-float load path is allowed (`vec4_ok`, see Alignment above)
+ * and the device's compute-unit count. Returns an sgemm_variant, or a
+ * negative status for invalid dimensions.
+ */
+int sgemm_select_variant(int transA, int transB, int M, int N, int K, int batch,
+                         int vec4_ok, int num_cus);
+
+/*
+ * sgemm_strided_batched with the kernel variant forced (testing and tuning):
+ * `variant` is an sgemm_variant; SGEMM_VARIANT_AUTO behaves exactly like
+ * sgemm_strided_batched. A 4-float variant requested for operands that do
+ * not meet its alignment, or an unknown variant, returns -18 (the position
+ * of `variant`).
+ */
+int sgemm_strided_batched_variant(int transA, int transB, int M, int N, int K,
+                                  float alpha, const float *A, int lda,
+                                               const float *B, int ldb,
+                                  float beta,        float *C, int ldc,
+                                  int batch, long long strideA, long long strideB,
+                                  long long strideC, int variant,
+                                  sgemm_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PRECISION_GEMM_AMD_SGEMM_H */

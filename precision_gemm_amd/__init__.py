@@ -1,0 +1,165 @@
+"""precision_gemm_amd — single-precision GEMM on MI355X (gfx950).
+
+A thin ctypes binding over ``libsgemm.so`` (built from ``csrc/sgemm.hip``;
+its C ABI is declared in ``include/sgemm.h``). The functions have the C
+names and argument order; they only marshal arguments (tensor -> device
+pointer, torch's current stream -> hipStream_t) and raise on a nonzero
+status. All arithmetic runs in the library's HIP kernels; there is no CPU or
+PyTorch fallback, and a missing library is an error.
+
+    C = alpha * op(A) @ op(B) + beta * C            (fp32, row-major)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = [
+    "SgemmError", "sgemm", "sgemm_strided_batched", "sgemm_strided_batched_variant",
+    "sgemm_status_string", "sgemm_select_variant", "matmul", "library_path",
+    "VARIANT_AUTO", "VARIANT_L256x128", "VARIANT_M128x128", "VARIANT_S64x64",
+    "VARIANT_S64x64_V1", "VARIANT_NAMES",
+]
+
+VARIANT_AUTO = -1
+VARIANT_L256x128 = 0
+VARIANT_M128x128 = 1
+VARIANT_S64x64 = 2
+VARIANT_S64x64_V1 = 3
+VARIANT_NAMES = {0: "L256x128", 1: "M128x128", 2: "S64x64", 3: "S64x64_V1"}
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_lib = None
+
+
+def library_path() -> str:
+    return os.path.join(_HERE, "libsgemm.so")
+
+
+class SgemmError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"sgemm status {status}: {message}")
+        self.status = status
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise ImportError(
+            f"{path} is missing: the HIP library must be built first "
+            "(python -c 'import __graft_entry__ as g; g.build()')")
+    lib = ctypes.CDLL(path)
+    i, f, p, ll = ctypes.c_int, ctypes.c_float, ctypes.c_void_p, ctypes.c_longlong
+    lib.sgemm.restype = i
+    lib.sgemm.argtypes = [i, i, i, i, i, f, p, i, p, i, f, p, i, p]
+    lib.sgemm_strided_batched.restype = i
+    lib.sgemm_strided_batched.argtypes = [i, i, i, i, i, f, p, i, p, i, f, p, i, i, ll, ll, ll, p]
+    lib.sgemm_strided_batched_variant.restype = i
+    lib.sgemm_strided_batched_variant.argtypes = [i, i, i, i, i, f, p, i, p, i, f, p, i, i,
+                                                  ll, ll, ll, i, p]
+    lib.sgemm_status_string.restype = ctypes.c_char_p
+    lib.sgemm_status_string.argtypes = [i]
+    lib.sgemm_select_variant.restype = i
+    lib.sgemm_select_variant.argtypes = [i, i, i, i, i, i, i, i]
+    _lib = lib
+    return lib
+
+
+def _ptr(x):
+    """Device pointer of a float32 GPU tensor, or an int / None passed through."""
+    if x is None or isinstance(x, int):
+        return x
+    if hasattr(x, "data_ptr"):
+        if not x.is_cuda:
+            raise TypeError("sgemm operands must be GPU tensors")
+        import torch
+        if x.dtype != torch.float32:
+            raise TypeError(f"sgemm operands must be float32, got {x.dtype}")
+        return x.data_ptr()
+    raise TypeError(f"cannot take a device pointer of {type(x).__name__}")
+
+
+def _stream(stream, *tensors):
+    if stream is not None:
+        return stream if isinstance(stream, int) else stream.cuda_stream
+    for t in tensors:
+        if hasattr(t, "data_ptr"):
+            import torch
+            return torch.cuda.current_stream(t.device).cuda_stream
+    return None
+
+
+def _check(status: int, check: bool) -> int:
+    if status != 0 and check:
+        raise SgemmError(status, sgemm_status_string(status))
+    return status
+
+
+def sgemm_status_string(status: int) -> str:
+    return _load().sgemm_status_string(int(status)).decode()
+
+
+def sgemm(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream=None,
+          check=True) -> int:
+    """C ABI ``sgemm``; A, B, C are float32 GPU tensors (or raw pointers)."""
+    st = _load().sgemm(int(transA), int(transB), M, N, K, float(alpha), _ptr(A), lda,
+                       _ptr(B), ldb, float(beta), _ptr(C), ldc, _stream(stream, A, B, C))
+    return _check(st, check)
+
+
+def sgemm_strided_batched(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
+                          batch, strideA, strideB, strideC, stream=None, check=True) -> int:
+    """C ABI ``sgemm_strided_batched``."""
+    st = _load().sgemm_strided_batched(int(transA), int(transB), M, N, K, float(alpha),
+                                       _ptr(A), lda, _ptr(B), ldb, float(beta), _ptr(C), ldc,
+                                       batch, strideA, strideB, strideC,
+                                       _stream(stream, A, B, C))
+    return _check(st, check)
+
+
+def sgemm_strided_batched_variant(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C,
+                                  ldc, batch, strideA, strideB, strideC, variant,
+                                  stream=None, check=True) -> int:
+    """C ABI ``sgemm_strided_batched_variant`` (kernel variant forced)."""
+    st = _load().sgemm_strided_batched_variant(
+        int(transA), int(transB), M, N, K, float(alpha), _ptr(A), lda, _ptr(B), ldb,
+        float(beta), _ptr(C), ldc, batch, strideA, strideB, strideC, int(variant),
+        _stream(stream, A, B, C))
+    return _check(st, check)
+
+
+def sgemm_select_variant(transA, transB, M, N, K, batch, vec4_ok, num_cus) -> int:
+    """C ABI ``sgemm_select_variant`` (host-side dispatch decision)."""
+    return _load().sgemm_select_variant(int(transA), int(transB), M, N, K, batch,
+                                        int(bool(vec4_ok)), num_cus)
+
+
+def matmul(A, B, C, alpha=1.0, beta=0.0, transA=False, transB=False, stream=None):
+    """In-place ``C = alpha*op(A)@op(B) + beta*C`` on 2-D (or 3-D, batched)
+    float32 GPU tensors whose last dimension is contiguous; the leading
+    dimensions are the tensors' row strides. Returns C."""
+    if A.dim() != B.dim() or A.dim() != C.dim() or A.dim() not in (2, 3):
+        raise ValueError("matmul takes three 2-D or three 3-D tensors")
+    for t in (A, B, C):
+        if t.stride(-1) != 1:
+            raise ValueError("the last dimension of every operand must be contiguous")
+    M, N = C.shape[-2], C.shape[-1]
+    K = A.shape[-2] if transA else A.shape[-1]
+    if (A.shape[-1] if transA else A.shape[-2]) != M:
+        raise ValueError("op(A) rows must equal C rows")
+    if (B.shape[-1] if transB else B.shape[-2]) != K or \
+            (B.shape[-2] if transB else B.shape[-1]) != N:
+        raise ValueError("op(B) must be K x N")
+    lda, ldb, ldc = (max(1, t.stride(-2)) for t in (A, B, C))
+    if A.dim() == 2:
+        sgemm(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream)
+    else:
+        batch = C.shape[0]
+        if A.shape[0] != batch or B.shape[0] != batch:
+            raise ValueError("batch sizes differ")
+        sgemm_strided_batched(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
+                              batch, A.stride(0), B.stride(0), C.stride(0), stream)
+    return C

@@ -1,0 +1,612 @@
+// libsgemm: single-precision GEMM for MI355X (gfx950, CDNA4).
+//
+//   C = alpha * op(A) @ op(B) + beta * C        (fp32, row-major)
+//
+// The operation is the SGEMM defined in "From 1% to 94% of cuBLAS, one kernel
+// at a time" (the SGEMM paragraph and its kernels' alpha/beta epilogue). The
+// structure follows the ideas that page builds up — block tiles staged in
+// on-chip memory (kernel 3), register tiles reused across many products
+// (kernels 4-5, 10), 128-bit loads (kernel 6), conflict-free shared-memory
+// layouts (kernels 7-8), double buffering (its closing list) — and those of
+// "Triton Optimization Reference (cuTile -> Triton)": an EVEN_K fast path
+// with a masked tail (section 1), transposes in the load addressing (section
+// 2), a (tiles, batch) grid with grouped tile order (section 3).
+//
+// How it maps onto CDNA4:
+//   * The register tile is a grid of v_mfma_f32_32x32x2_f32 products: full
+//     fp32 inputs, fp32 accumulation, 64 lanes per wave. A wave owns a
+//     (32*TM) x (32*TN) piece of the workgroup tile.
+//   * Each K-step the workgroup copies op(A) (BM x BK) and op(B) (BK x BN)
+//     from global memory to LDS with 16-byte buffer loads along whichever
+//     dimension is contiguous in memory, so a transposed operand costs
+//     nothing extra: only the address map and the LDS layout change.
+//       - k-contiguous operand (A with transA=0, B with transB=1): LDS rows
+//         of BK floats, one per output row/column, with the 16-byte column
+//         XOR-swizzled by row so that 128-bit reads of eight consecutive
+//         rows hit distinct banks;
+//       - outer-contiguous operand (A with transA=1, B with transB=0): LDS
+//         rows of BM (or BN) floats, one per k, read one float per lane.
+//   * The k index is permuted inside every group of 8: MFMA step j of a
+//     group feeds k = j to lanes 0-31 and k = 4+j to lanes 32-63, so one
+//     128-bit LDS read of a k-contiguous row supplies four consecutive MFMA
+//     steps. Both operands use the same permutation, so the sum over k is
+//     unchanged (only its fp32 rounding order differs).
+//   * Masking is free: every load and store goes through a buffer resource
+//     whose range ends at the operand's last element; a lane outside M, N or
+//     K gets a byte offset >= 2^31, which the hardware turns into a zero load
+//     or a dropped store. The resource base advances each K-step, so the
+//     per-lane offsets are fixed for the whole loop and stay below 2^31.
+//   * LDS is double-buffered with one barrier per K-step; the next step's
+//     global loads are in flight while the current step's MFMAs run.
+//   * Workgroups are consecutive-ID round-robin over the 8 XCDs; tile IDs are
+//     remapped so that each XCD (and its L2) gets a contiguous run of tiles,
+//     which are then ordered in groups of GROUP_M tile rows.
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <stdint.h>
+
+#include "sgemm.h"
+
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr uint32_t kOOB = 0x80000000u;     // any byte offset >= this is out of range
+constexpr uint32_t kMaxRange = 0x7fffffffu; // largest buffer range used
+constexpr int kRsrcWord3 = 0x00020000;     // gfx9 raw buffer, 32-bit data format
+constexpr int kNumXcd = 8;                 // MI355X: 8 XCDs x 32 CUs
+constexpr int kMaxLd = (1 << 21) - 1;      // keeps (255*ld + 256)*4 < 2^31
+
+struct Params {
+    const float *A;
+    const float *B;
+    float *C;
+    int M, N, K;
+    int lda, ldb, ldc;
+    long long sA, sB, sC;
+    float alpha, beta;
+    int batch;       // batch items covered by this launch
+    int tiles_m, tiles_n;
+    int group_m;
+};
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const float *base, long long elems)
+{
+    long long bytes = elems * 4;
+    uint32_t range = bytes <= 0 ? 0u : (bytes > (long long)kMaxRange ? kMaxRange : (uint32_t)bytes);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(base), (short)0, (int)range,
+                                             kRsrcWord3);
+}
+
+__device__ __forceinline__ f32x4 load4(__amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+__device__ __forceinline__ float load1(__amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+
+__device__ __forceinline__ void store1(__amdgpu_buffer_rsrc_t r, uint32_t off, float v)
+{
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, v), r, off, 0, 0);
+}
+
+// ---------------------------------------------------------------------------
+// One operand's K-step tile: global -> registers -> LDS, and LDS -> MFMA
+// operands. KC: k is the contiguous dimension of the stored operand.
+// BO: outer extent of the tile (BM for A, BN for B). VEC: floats per load.
+// ---------------------------------------------------------------------------
+template <bool KC, int BO, int BK, int NT, int VEC>
+struct Operand {
+    static constexpr int PAD = 0;                        // outer-contiguous row padding
+    static constexpr int ROW = KC ? BK : BO + PAD;       // LDS row length (floats)
+    static constexpr int STAGE = KC ? BO * BK : BK * (BO + PAD);
+    static constexpr int C4 = KC ? BK / 4 : BO / 4;      // 16-byte chunks per stored tile row
+    static constexpr int SLOTS = BO * BK / (4 * NT);     // 16-byte chunks per thread
+    static constexpr int EPS = VEC == 4 ? 1 : 4;         // byte offsets kept per slot
+    static constexpr int NOFF = SLOTS * EPS;
+    static constexpr int SWZ_ROWS = BK >= 32 ? 1 : 32 / BK; // rows sharing one 32-bank sweep
+    static_assert(BO * BK % (4 * NT) == 0 && SLOTS >= 1, "tile does not split evenly");
+    static_assert(BK % 8 == 0, "BK must be a multiple of 8");
+    static_assert(VEC == 4 || VEC == 1, "VEC");
+
+    const float *X;   // this batch item's operand
+    long long ld;
+    long long total;  // elements from X to one past the last stored element
+    int O, K;         // outer extent and K of the product
+    int o0;           // first outer index of this tile
+    uint32_t off[NOFF];
+
+    __device__ __forceinline__ static int swz(int r) { return (r / SWZ_ROWS) % (BK / 4); }
+
+    // Position of 16-byte chunk (row r, chunk c4) of the K-step tile in LDS.
+    __device__ __forceinline__ static int lds_index(int r, int c4)
+    {
+        return KC ? r * BK + 4 * (c4 ^ swz(r)) : r * ROW + 4 * c4;
+    }
+
+    __device__ __forceinline__ void init(int tid)
+    {
+#pragma unroll
+        for (int s = 0; s < SLOTS; ++s) {
+            const int f = tid + s * NT, r = f / C4, c4 = f % C4;
+            const long long elem = (long long)r * ld + 4 * c4;
+#pragma unroll
+            for (int e = 0; e < EPS; ++e) {
+                // KC: row r is outer index o0+r and the chunk runs along k;
+                // otherwise row r is a k index and the chunk runs along outer.
+                const bool ok = KC ? (o0 + r < O) : (o0 + 4 * c4 + e < O);
+                off[s * EPS + e] = ok ? (uint32_t)((elem + e) * 4) : kOOB;
+            }
+        }
+    }
+
+    // Issue the loads of the K-step starting at k0 into regs.
+    template <bool TAIL>
+    __device__ __forceinline__ void load(int tid, int k0, f32x4 (&regs)[SLOTS]) const
+    {
+        const long long base = KC ? (long long)o0 * ld + k0 : (long long)k0 * ld + o0;
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(X + base, total - base);
+#pragma unroll
+        for (int s = 0; s < SLOTS; ++s) {
+            const int f = tid + s * NT, r = f / C4, c4 = f % C4;
+            if (VEC == 4) {
+                uint32_t o = off[s];
+                if (TAIL && !(KC ? (k0 + 4 * c4 < K) : (k0 + r < K)))
+                    o |= kOOB;
+                regs[s] = load4(rs, o);
+            } else {
+                f32x4 v;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    uint32_t o = off[s * 4 + e];
+                    if (TAIL && !(KC ? (k0 + 4 * c4 + e < K) : (k0 + r < K)))
+                        o |= kOOB;
+                    v[e] = load1(rs, o);
+                }
+                regs[s] = v;
+            }
+        }
+    }
+
+    __device__ __forceinline__ static void store(float *lds, int tid, const f32x4 (&regs)[SLOTS])
+    {
+#pragma unroll
+        for (int s = 0; s < SLOTS; ++s) {
+            const int f = tid + s * NT, r = f / C4, c4 = f % C4;
+            *reinterpret_cast<f32x4 *>(lds + lds_index(r, c4)) = regs[s];
+        }
+    }
+
+    // MFMA operands of k-group q (8 k values) for the 32-row slab at outer
+    // offset w (inside the tile): v[j] feeds MFMA step j of the group.
+    __device__ __forceinline__ static f32x4 frag(const float *lds, int w, int q, int lane)
+    {
+        const int o = w + (lane & 31), g = lane >> 5;
+        if (KC) {
+            return *reinterpret_cast<const f32x4 *>(lds + lds_index(o, 2 * q + g));
+        } else {
+            f32x4 v;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                v[j] = lds[(8 * q + 4 * g + j) * ROW + o];
+            return v;
+        }
+    }
+};
+
+// Flat workgroup id -> (batch item, tile row, tile column).
+__device__ __forceinline__ void tile_of(const Params &p, int &b, int &tm, int &tn)
+{
+    const int num = gridDim.x * gridDim.y;
+    const int pid = blockIdx.y * gridDim.x + blockIdx.x;
+    // Workgroup pid runs on XCD pid % 8; give each XCD a contiguous range.
+    const int xcd = pid % kNumXcd, local = pid / kNumXcd;
+    const int q = num / kNumXcd, r = num % kNumXcd;
+    const int logical = xcd < r ? xcd * (q + 1) + local : r * (q + 1) + (xcd - r) * q + local;
+    const int per_batch = p.tiles_m * p.tiles_n;
+    b = logical / per_batch;
+    const int t = logical % per_batch;
+    // Grouped order: GROUP_M tile rows are walked column by column.
+    const int in_group = p.group_m * p.tiles_n;
+    const int first_m = (t / in_group) * p.group_m;
+    const int gsize = min(p.tiles_m - first_m, p.group_m);
+    tm = first_m + (t % in_group) % gsize;
+    tn = (t % in_group) / gsize;
+}
+
+template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int MIN_WAVES_PER_EU,
+          bool A_KC, bool B_KC, bool EVEN_K, int VEC>
+__global__ void
+__attribute__((amdgpu_flat_work_group_size(64 * WAVES_M * WAVES_N, 64 * WAVES_M * WAVES_N),
+               amdgpu_waves_per_eu(MIN_WAVES_PER_EU)))
+sgemm_mfma_kernel(Params p)
+{
+    constexpr int NT = 64 * WAVES_M * WAVES_N;
+    constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
+    constexpr int TM = WM / 32, TN = WN / 32;
+    static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tile must be a multiple of 32");
+    using OpA = Operand<A_KC, BM, BK, NT, VEC>;
+    using OpB = Operand<B_KC, BN, BK, NT, VEC>;
+
+    // Two stages, each holding the A tile followed by the B tile.
+    constexpr int STAGE = OpA::STAGE + OpB::STAGE;
+    __shared__ __attribute__((aligned(16))) float lds[2 * STAGE];
+
+    int b, tile_m, tile_n;
+    tile_of(p, b, tile_m, tile_n);
+    const int m0 = tile_m * BM, n0 = tile_n * BN;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm0 = (wave % WAVES_M) * WM, wn0 = (wave / WAVES_M) * WN;
+
+    OpA opa;
+    opa.X = p.A + b * p.sA;
+    opa.ld = p.lda;
+    opa.total = A_KC ? (long long)(p.M - 1) * p.lda + p.K : (long long)(p.K - 1) * p.lda + p.M;
+    opa.O = p.M;
+    opa.K = p.K;
+    opa.o0 = m0;
+    opa.init(tid);
+    OpB opb;
+    opb.X = p.B + b * p.sB;
+    opb.ld = p.ldb;
+    opb.total = B_KC ? (long long)(p.N - 1) * p.ldb + p.K : (long long)(p.K - 1) * p.ldb + p.N;
+    opb.O = p.N;
+    opb.K = p.K;
+    opb.o0 = n0;
+    opb.init(tid);
+
+    f32x16 acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+            acc[i][j] = f32x16{};
+
+    f32x4 ra[OpA::SLOTS], rb[OpB::SLOTS];
+    const int nsteps = (p.K + BK - 1) / BK;
+
+    auto load_step = [&](int s) {
+        if (!EVEN_K && s == nsteps - 1) {
+            opa.template load<true>(tid, s * BK, ra);
+            opb.template load<true>(tid, s * BK, rb);
+        } else {
+            opa.template load<false>(tid, s * BK, ra);
+            opb.template load<false>(tid, s * BK, rb);
+        }
+    };
+
+    load_step(0);
+    OpA::store(lds, tid, ra);
+    OpB::store(lds + OpA::STAGE, tid, rb);
+    if (nsteps > 1)
+        load_step(1);
+    __syncthreads();
+
+    for (int s = 0; s < nsteps; ++s) {
+        const float *la = lds + (s & 1) * STAGE;
+        const float *lb = la + OpA::STAGE;
+#pragma unroll
+        for (int q = 0; q < BK / 8; ++q) {
+            f32x4 fa[TM], fb[TN];
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+                fa[i] = OpA::frag(la, wm0 + 32 * i, q, lane);
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+                fb[j] = OpB::frag(lb, wn0 + 32 * j, q, lane);
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+                for (int i = 0; i < TM; ++i)
+#pragma unroll
+                    for (int j = 0; j < TN; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[i][kk], fb[j][kk],
+                                                                          acc[i][j], 0, 0, 0);
+        }
+        if (s + 1 < nsteps) {
+            float *na = lds + ((s + 1) & 1) * STAGE;
+            OpA::store(na, tid, ra);
+            OpB::store(na + OpA::STAGE, tid, rb);
+            if (s + 2 < nsteps)
+                load_step(s + 2);
+        }
+        __syncthreads();
+    }
+
+    // Epilogue: C = alpha * acc + beta * C, lanes outside M x N dropped.
+    // Accumulator register v of lane l holds row 8*(v/4) + 4*(l/32) + v%4,
+    // column l%32 of its 32 x 32 product.
+    float *Cb = p.C + b * p.sC;
+    const long long cbase = (long long)m0 * p.ldc + n0;
+    const __amdgpu_buffer_rsrc_t rc =
+        make_rsrc(Cb + cbase, (long long)(p.M - 1) * p.ldc + p.N - cbase);
+    const int g = lane >> 5;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            const int col = wn0 + 32 * j + (lane & 31);
+            const bool col_ok = n0 + col < p.N;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int row = wm0 + 32 * i + 8 * (v >> 2) + 4 * g + (v & 3);
+                const uint32_t off = (col_ok && m0 + row < p.M)
+                                         ? (uint32_t)(((long long)row * p.ldc + col) * 4)
+                                         : kOOB;
+                float out = p.alpha * acc[i][j][v];
+                if (p.beta != 0.0f)
+                    out += p.beta * load1(rc, off);
+                store1(rc, off, out);
+            }
+        }
+    }
+}
+
+// C = beta * C over the M x N window of every batch item (alpha == 0 or K == 0).
+__global__ void __launch_bounds__(256) sgemm_scale_kernel(float *C, int M, int N, int ldc,
+                                                          long long sC, int batch, float beta)
+{
+    const long long per = (long long)M * N;
+    const long long total = per * batch;
+    for (long long e = blockIdx.x * 256LL + threadIdx.x; e < total;
+         e += (long long)gridDim.x * 256) {
+        const long long b = e / per, r = (e % per) / N, c = e % N;
+        float *x = C + b * sC + r * ldc + c;
+        *x = beta == 0.0f ? 0.0f : beta * *x;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Host side
+// ---------------------------------------------------------------------------
+
+typedef void (*KernelFn)(Params);
+
+struct VariantInfo {
+    int bm, bn, threads, vec;
+    KernelFn fn[2][2][2]; // [transA][transB][even_k]
+};
+
+template <int BM, int BN, int BK, int WM_, int WN_, int MW, int VEC>
+constexpr VariantInfo make_variant()
+{
+    return VariantInfo{
+        BM, BN, 64 * WM_ * WN_, VEC,
+        {{{sgemm_mfma_kernel<BM, BN, BK, WM_, WN_, MW, true, false, false, VEC>,
+           sgemm_mfma_kernel<BM, BN, BK, WM_, WN_, MW, true, false, true, VEC>},
+          {sgemm_mfma_kernel<BM, BN, BK, WM_, WN_, MW, true, true, false, VEC>,
+           sgemm_mfma_kernel<BM, BN, BK, WM_, WN_, MW, true, true, true, VEC>}},
+         {{sgemm_mfma_kernel<BM, BN, BK, WM_, WN_, MW, false, false, false, VEC>,
+           sgemm_mfma_kernel<BM, BN, BK, WM_, WN_, MW, false, false, true, VEC>},
+          {sgemm_mfma_kernel<BM, BN, BK, WM_, WN_, MW, false, true, false, VEC>,
+           sgemm_mfma_kernel<BM, BN, BK, WM_, WN_, MW, false, true, true, VEC>}}}};
+}
+
+constexpr int kBK = 16;
+
+const VariantInfo kVariants[SGEMM_VARIANT_COUNT] = {
+    make_variant<256, 128, kBK, 2, 2, 2, 4>(), // SGEMM_VARIANT_L256x128
+    make_variant<128, 128, kBK, 2, 2, 2, 4>(), // SGEMM_VARIANT_M128x128
+    make_variant<64, 64, kBK, 2, 2, 4, 4>(),   // SGEMM_VARIANT_S64x64
+    make_variant<64, 64, kBK, 2, 2, 4, 1>(),   // SGEMM_VARIANT_S64x64_V1
+};
+
+long long ceil_div(long long a, long long b) { return (a + b - 1) / b; }
+
+int num_cus_of_current_device(int *out)
+{
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return (int)e;
+    if (dev >= 0 && dev < 64) {
+        int v = cache[dev].load(std::memory_order_relaxed);
+        if (v > 0) {
+            *out = v;
+            return 0;
+        }
+    }
+    int cus = 0;
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess)
+        return (int)e;
+    if (dev >= 0 && dev < 64)
+        cache[dev].store(cus, std::memory_order_relaxed);
+    *out = cus;
+    return 0;
+}
+
+int validate(int tA, int tB, int M, int N, int K, const float *A, int lda, const float *B,
+             int ldb, const float *C, int ldc, int batch, long long sA, long long sB,
+             long long sC, float alpha, float beta)
+{
+    if (tA != 0 && tA != 1) return -1;
+    if (tB != 0 && tB != 1) return -2;
+    if (M < 0) return -3;
+    if (N < 0) return -4;
+    if (K < 0) return -5;
+    const int rowA = tA ? M : K, rowB = tB ? K : N;
+    if (lda < (rowA > 1 ? rowA : 1) || lda > kMaxLd) return -8;
+    if (ldb < (rowB > 1 ? rowB : 1) || ldb > kMaxLd) return -10;
+    if (ldc < (N > 1 ? N : 1) || ldc > kMaxLd) return -13;
+    if (batch < 0) return -14;
+    if (sA < 0) return -15;
+    if (sB < 0) return -16;
+    if (sC < 0) return -17;
+    const bool work = M > 0 && N > 0 && batch > 0;
+    const bool product = work && K > 0 && alpha != 0.0f;
+    const bool touch_c = work && (product || beta != 1.0f);
+    if (product && A == nullptr) return -7;
+    if (product && B == nullptr) return -9;
+    if (touch_c && C == nullptr) return -12;
+    return 0;
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+} // namespace
+
+extern "C" int sgemm_select_variant(int transA, int transB, int M, int N, int K, int batch,
+                                    int vec4_ok, int num_cus)
+{
+    if (transA != 0 && transA != 1) return -1;
+    if (transB != 0 && transB != 1) return -2;
+    if (M < 0) return -3;
+    if (N < 0) return -4;
+    if (K < 0) return -5;
+    if (batch < 0) return -14;
+    if (!vec4_ok)
+        return SGEMM_VARIANT_S64x64_V1;
+    if (num_cus < 1)
+        num_cus = 1;
+    // Largest tile whose grid still gives every CU a workgroup; the large
+    // tiles need two resident workgroups per CU to cover their barriers.
+    const long long tiles_l = ceil_div(M, 256) * ceil_div(N, 128) * batch;
+    const long long tiles_m = ceil_div(M, 128) * ceil_div(N, 128) * batch;
+    if (tiles_l >= 2LL * num_cus)
+        return SGEMM_VARIANT_L256x128;
+    if (tiles_m >= 2LL * num_cus)
+        return SGEMM_VARIANT_M128x128;
+    return SGEMM_VARIANT_S64x64;
+}
+
+extern "C" int sgemm_strided_batched_variant(int transA, int transB, int M, int N, int K,
+                                             float alpha, const float *A, int lda,
+                                             const float *B, int ldb, float beta, float *C,
+                                             int ldc, int batch, long long strideA,
+                                             long long strideB, long long strideC, int variant,
+                                             sgemm_stream_t stream)
+{
+    int st = validate(transA, transB, M, N, K, A, lda, B, ldb, C, ldc, batch, strideA, strideB,
+                      strideC, alpha, beta);
+    if (st != 0)
+        return st;
+    if (variant < SGEMM_VARIANT_AUTO || variant >= SGEMM_VARIANT_COUNT)
+        return -18;
+    if (M == 0 || N == 0 || batch == 0)
+        return 0;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+
+    if (K == 0 || alpha == 0.0f) {
+        if (beta == 1.0f)
+            return 0;
+        const long long total = (long long)M * N * batch;
+        const long long blocks = ceil_div(total, 256) < 8192 ? ceil_div(total, 256) : 8192;
+        void *args[] = {&C, &M, &N, &ldc, &strideC, &batch, &beta};
+        return (int)hipLaunchKernel((const void *)sgemm_scale_kernel, dim3((unsigned)blocks),
+                                    dim3(256), args, 0, s);
+    }
+
+    // 16-byte loads need aligned bases, ld and batch strides, and whole
+    // 4-float chunks along each operand's contiguous dimension.
+    const bool a_kc = transA == 0, b_kc = transB == 1;
+    const bool vec4_ok = aligned16(A) && aligned16(B) && lda % 4 == 0 && ldb % 4 == 0 &&
+                         strideA % 4 == 0 && strideB % 4 == 0 &&
+                         (a_kc ? K % 4 == 0 : M % 4 == 0) && (b_kc ? K % 4 == 0 : N % 4 == 0);
+    if (variant == SGEMM_VARIANT_AUTO) {
+        int cus = 0;
+        st = num_cus_of_current_device(&cus);
+        if (st != 0)
+            return st;
+        variant = sgemm_select_variant(transA, transB, M, N, K, batch, vec4_ok ? 1 : 0, cus);
+        if (variant < 0)
+            return variant;
+    } else if (kVariants[variant].vec == 4 && !vec4_ok) {
+        return -18;
+    }
+
+    const VariantInfo &vi = kVariants[variant];
+    const int even_k = K % kBK == 0 ? 1 : 0;
+    Params p;
+    p.A = A;
+    p.B = B;
+    p.C = C;
+    p.M = M;
+    p.N = N;
+    p.K = K;
+    p.lda = lda;
+    p.ldb = ldb;
+    p.ldc = ldc;
+    p.sA = strideA;
+    p.sB = strideB;
+    p.sC = strideC;
+    p.alpha = alpha;
+    p.beta = beta;
+    p.tiles_m = (int)ceil_div(M, vi.bm);
+    p.tiles_n = (int)ceil_div(N, vi.bn);
+    p.group_m = 8;
+    const long long per_batch = (long long)p.tiles_m * p.tiles_n;
+    // Keep one launch's workgroup count within 2^31 and its batch axis within 65535.
+    long long max_items = ((1LL << 31) - 1) / per_batch;
+    if (max_items > 65535)
+        max_items = 65535;
+    if (max_items < 1)
+        return -3;
+    KernelFn fn = vi.fn[transA][transB][even_k];
+    for (long long b0 = 0; b0 < batch; b0 += max_items) {
+        const long long nb = batch - b0 < max_items ? batch - b0 : max_items;
+        Params q = p;
+        q.A = A + b0 * strideA;
+        q.B = B + b0 * strideB;
+        q.C = C + b0 * strideC;
+        q.batch = (int)nb;
+        void *args[] = {&q};
+        hipError_t e = hipLaunchKernel((const void *)fn, dim3((unsigned)per_batch, (unsigned)nb),
+                                       dim3(vi.threads), args, 0, s);
+        if (e != hipSuccess)
+            return (int)e;
+    }
+    return 0;
+}
+
+extern "C" int sgemm_strided_batched(int transA, int transB, int M, int N, int K, float alpha,
+                                     const float *A, int lda, const float *B, int ldb,
+                                     float beta, float *C, int ldc, int batch, long long strideA,
+                                     long long strideB, long long strideC, sgemm_stream_t stream)
+{
+    return sgemm_strided_batched_variant(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C,
+                                         ldc, batch, strideA, strideB, strideC,
+                                         SGEMM_VARIANT_AUTO, stream);
+}
+
+extern "C" int sgemm(int transA, int transB, int M, int N, int K, float alpha, const float *A,
+                     int lda, const float *B, int ldb, float beta, float *C, int ldc,
+                     sgemm_stream_t stream)
+{
+    return sgemm_strided_batched(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, 1,
+                                 0, 0, 0, stream);
+}
+
+extern "C" const char *sgemm_status_string(int status)
+{
+    switch (status) {
+    case 0: return "success";
+    case -1: return "invalid argument 1 (transA must be 0 or 1)";
+    case -2: return "invalid argument 2 (transB must be 0 or 1)";
+    case -3: return "invalid argument 3 (M < 0)";
+    case -4: return "invalid argument 4 (N < 0)";
+    case -5: return "invalid argument 5 (K < 0)";
+    case -7: return "invalid argument 7 (A is NULL)";
+    case -8: return "invalid argument 8 (lda below the stored row length or >= 2^21)";
+    case -9: return "invalid argument 9 (B is NULL)";
+    case -10: return "invalid argument 10 (ldb below the stored row length or >= 2^21)";
+    case -12: return "invalid argument 12 (C is NULL)";
+    case -13: return "invalid argument 13 (ldc < max(1, N) or >= 2^21)";
+    case -14: return "invalid argument 14 (batch < 0)";
+    case -15: return "invalid argument 15 (strideA < 0)";
+    case -16: return "invalid argument 16 (strideB < 0)";
+    case -17: return "invalid argument 17 (strideC < 0)";
+    case -18: return "invalid argument 18 (unknown variant, or a 4-float variant for unaligned operands)";
+    default: break;
+    }
+    if (status < 0)
+        return "invalid argument";
+    return hipGetErrorString(static_cast<hipError_t>(status));
+}

@@ -1,0 +1,320 @@
+"""GPU parity: the HIP library against the CPU oracle, through the C ABI.
+
+Floating-point cases must meet the acceptance bound
+|C_gpu - ref| <= 2e-6 * max(K,1) * (|alpha| * S + |beta| * |C_in|) elementwise.
+Integer-valued cases (entries in [-3, 3], alpha/beta in {1, 2, -1, 0.5})
+make every partial sum exact in fp32, so there the GPU must equal the oracle
+bit for bit whatever the summation order.
+
+Every launch also checks that nothing outside the M x N windows of C moved:
+the device buffer carries guard bands before and after it, and ld padding
+and gaps between batch items must keep their input bits.
+"""
+import itertools
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from workloads import Workload
+
+pytestmark = pytest.mark.gpu
+
+GUARD = 64  # floats of canary before and after each device buffer (keeps 256-B alignment)
+
+
+@pytest.fixture(scope="module")
+def env():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import precision_gemm_amd as pg
+    pg._load()
+    return torch, pg
+
+
+def log(msg):
+    sys.stdout.write(msg + "\n")
+    sys.stdout.flush()
+
+
+def c_window_mask(w: Workload, n: int) -> np.ndarray:
+    """Flat positions of C that the call may write."""
+    mask = np.zeros(n, bool)
+    if w.M == 0 or w.N == 0:
+        return mask
+    for b in range(w.batch):
+        base = b * w.SC
+        rows = base + np.arange(w.M)[:, None] * w.LDC + np.arange(w.N)[None, :]
+        mask[rows.reshape(-1)] = True
+    return mask
+
+
+def c_items(flat: np.ndarray, w: Workload) -> np.ndarray:
+    """(batch, M, N) view of a flat C buffer."""
+    out = np.empty((w.batch, w.M, w.N), flat.dtype)
+    for b in range(w.batch):
+        out[b] = np.lib.stride_tricks.as_strided(
+            flat[b * w.SC:], (w.M, w.N), (w.LDC * flat.itemsize, flat.itemsize))
+    return out
+
+
+def run_gpu(env, w: Workload, A, B, C, variant=-1, c_offset=0):
+    """Launch on cuda:0; returns (status, C after the call as a flat array)."""
+    torch, pg = env
+    dev = torch.device("cuda:0")
+
+    def put(x, extra=0):
+        buf = torch.full((x.size + 2 * GUARD + extra,), -7.25, dtype=torch.float32, device=dev)
+        buf[GUARD + extra:GUARD + extra + x.size] = torch.from_numpy(x).to(dev)
+        return buf, GUARD + extra
+
+    dA, oa = put(A)
+    dB, ob = put(B)
+    dC, oc = put(C, c_offset)
+    pa, pb, pc = (t.data_ptr() + 4 * o for t, o in ((dA, oa), (dB, ob), (dC, oc)))
+    st = pg.sgemm_strided_batched_variant(
+        w.trans_a, w.trans_b, w.M, w.N, w.K, w.alpha, pa, w.LDA, pb, w.LDB, w.beta, pc, w.LDC,
+        w.batch, w.SA, w.SB, w.SC, variant, stream=torch.cuda.current_stream(dev).cuda_stream,
+        check=False)
+    torch.cuda.synchronize(dev)
+    whole = dC.cpu().numpy()
+    guard_ok = (np.all(whole[:oc] == np.float32(-7.25)) and
+                np.all(whole[oc + C.size:] == np.float32(-7.25)))
+    assert guard_ok, "a guard band around C was overwritten"
+    return st, whole[oc:oc + C.size]
+
+
+def check_against_oracle(w, A, B, C, got, exact=False, rows=None, batches=None):
+    ref, S = oracle.sgemm_rows(w.trans_a, w.trans_b, w.M, w.N, w.K, w.alpha, A, w.LDA, B,
+                               w.LDB, w.beta, C, w.LDC, batch=w.batch, stride_a=w.SA,
+                               stride_b=w.SB, stride_c=w.SC, rows=rows, batches=batches)
+    r0, r1 = rows or (0, w.M)
+    b0, b1 = batches or (0, w.batch)
+    g = c_items(got, w)[b0:b1, r0:r1]
+    cin = c_items(C, w)[b0:b1, r0:r1]
+    if exact:
+        want = ref.astype(np.float32)
+        assert np.array_equal(ref, want.astype(np.float64)), "integer case not exact in fp32"
+        bad = np.argwhere(g != want)
+        assert bad.size == 0, f"{w}: {len(bad)} mismatches, first {bad[:3].tolist()} " \
+                              f"got {g[tuple(bad[0])]} want {want[tuple(bad[0])]}"
+        return None
+    rep = oracle.bound_check(g, ref, S, cin, w.alpha, w.beta, w.K)
+    assert rep.ok, f"{w.name}: {rep}"
+    return rep
+
+
+def check_untouched(w, C, got):
+    mask = c_window_mask(w, C.size)
+    assert np.array_equal(got[~mask].view(np.uint32), C[~mask].view(np.uint32)), \
+        "C changed outside its M x N windows"
+
+
+# ------------------------------------------------------------------ the five workloads
+
+@pytest.mark.parametrize("name", [w.name for w in workloads.CONFIGS])
+def test_workload_parity(env, name):
+    """Full-size workloads in the launch configuration the benchmark times
+    (automatic variant). Small ones are checked whole; the 4092^3 product on
+    sampled row bands (first, middle, the ragged last band) and the batched
+    one on sampled batch items."""
+    w = workloads.BY_NAME[name]
+    A, B, C = workloads.make_inputs(w)
+    log(f"[parity] {name} M={w.M} N={w.N} K={w.K} batch={w.batch}")
+    st, got = run_gpu(env, w, A, B, C)
+    assert st == 0
+    check_untouched(w, C, got)
+    if name == "sgemm_4092":
+        for rows in ((0, 96), (2000, 2064), (w.M - 100, w.M)):
+            rep = check_against_oracle(w, A, B, C, got, rows=rows)
+            log(f"  rows {rows}: {rep}")
+    elif name.startswith("bmm"):
+        for b in (0, 37, w.batch - 1):
+            rep = check_against_oracle(w, A, B, C, got, batches=(b, b + 1))
+            log(f"  batch {b}: {rep}")
+    else:
+        rep = check_against_oracle(w, A, B, C, got)
+        log(f"  {rep}")
+
+
+def test_workload_4092_sampled_elements(env):
+    """Random elements across the whole 4092^3 output, each recomputed alone."""
+    w = workloads.HEADLINE
+    A, B, C = workloads.make_inputs(w)
+    st, got = run_gpu(env, w, A, B, C)
+    assert st == 0
+    rng = np.random.default_rng(123)
+    n = 4000
+    is_ = np.concatenate([rng.integers(0, w.M, n), np.full(64, w.M - 1), np.arange(64)])
+    js = np.concatenate([rng.integers(0, w.N, n), rng.integers(0, w.N, 64),
+                         np.full(64, w.N - 1)])
+    bs = np.zeros_like(is_)
+    ref, S = oracle.sgemm_elements(0, 0, w.K, w.alpha, A, w.LDA, B, w.LDB, w.beta, C, w.LDC,
+                                   bs, is_, js)
+    g = got[is_ * w.LDC + js]
+    cin = C[is_ * w.LDC + js]
+    rep = oracle.bound_check(g, ref, S, cin, w.alpha, w.beta, w.K)
+    log(f"  sampled elements: {rep}")
+    assert rep.ok
+
+
+# ------------------------------------------------------------------ variant sweeps
+
+SIZES = [1, 2, 3, 4, 5, 7, 8, 15, 16, 17, 31, 32, 33, 63, 64, 65, 127, 128, 129, 255, 256, 257]
+# multiples of 4 (the 4-float variants' domain), ragged against every tile size
+SIZES4 = [4, 8, 12, 16, 20, 28, 32, 36, 60, 64, 68, 124, 128, 132, 252, 256, 260]
+
+
+def sweep_shapes(n, seed):
+    rng = np.random.default_rng(seed)
+    shapes = {(1, 1, 1), (4, 4, 4), (257, 257, 257), (256, 128, 16), (255, 129, 33),
+              (260, 132, 20)}
+    while len(shapes) < n:
+        pool = SIZES4 if len(shapes) % 2 else SIZES
+        shapes.add(tuple(int(x) for x in rng.choice(pool, 3)))
+    return sorted(shapes)
+
+
+def vec4_possible(w):
+    a_kc, b_kc = w.trans_a == 0, w.trans_b == 1
+    return ((w.K % 4 == 0) if a_kc else (w.M % 4 == 0)) and \
+           ((w.K % 4 == 0) if b_kc else (w.N % 4 == 0)) and \
+           w.LDA % 4 == 0 and w.LDB % 4 == 0 and w.SA % 4 == 0 and w.SB % 4 == 0
+
+
+@pytest.mark.parametrize("variant", [0, 1, 2, 3])
+def test_integer_sweep_bitwise(env, variant):
+    """Every forced variant x transpose pair over ragged sizes, integer inputs:
+    bitwise equality with the oracle."""
+    _, pg = env
+    ab = [(1.0, 0.0), (2.0, 1.0), (-1.0, 0.5), (0.5, 2.0)]
+    n_run = 0
+    for idx, (M, N, K) in enumerate(sweep_shapes(40, seed=variant)):
+        for tA, tB in itertools.product([0, 1], repeat=2):
+            alpha, beta = ab[(idx + 2 * tA + tB) % len(ab)]
+            pad = 4 if idx % 3 == 0 else 0
+            w = Workload(f"int{M}x{N}x{K}", tA, tB, M, N, K, alpha, beta, seed=idx,
+                         dist="int3",
+                         lda=(M if tA else K) + pad, ldb=(K if tB else N) + pad, ldc=N + pad)
+            A, B, C = workloads.make_inputs(w)
+            st, got = run_gpu(env, w, A, B, C, variant=variant)
+            if pg.VARIANT_NAMES[variant] != "S64x64_V1" and not vec4_possible(w):
+                assert st == -18, (w, st)
+                continue
+            assert st == 0, (w, st)
+            check_against_oracle(w, A, B, C, got, exact=True)
+            check_untouched(w, C, got)
+            n_run += 1
+    log(f"  variant {variant}: {n_run} bitwise cases")
+    assert n_run > 20
+
+
+@pytest.mark.parametrize("variant", [0, 1, 2, 3])
+def test_float_sweep_bound(env, variant):
+    """Random fp32 inputs, several tiles plus ragged tails in every dimension,
+    all transposes, padded leading dimensions, batches with gaps."""
+    shapes = [(300, 200, 100), (513, 257, 77), (96, 160, 520), (640, 384, 36)]
+    for (M, N, K), (tA, tB) in itertools.product(shapes, itertools.product([0, 1], repeat=2)):
+        w = Workload(f"f{M}x{N}x{K}", tA, tB, M, N, K, 0.75, -1.5, seed=M + N + K,
+                     dist="normal", batch=2, lda=(M if tA else K) + 8,
+                     ldb=(K if tB else N) + 4, ldc=N + 12)
+        w = Workload(**{**w.__dict__, "stride_a": w.SA + 16, "stride_b": w.SB + 4,
+                        "stride_c": w.SC + 20})
+        A, B, C = workloads.make_inputs(w)
+        st, got = run_gpu(env, w, A, B, C, variant=variant)
+        if variant != 3 and not vec4_possible(w):
+            assert st == -18
+            continue
+        assert st == 0, (w, st)
+        check_against_oracle(w, A, B, C, got)
+        check_untouched(w, C, got)
+
+
+# ------------------------------------------------------------------ special cases
+
+def test_beta_zero_ignores_nan_in_c(env):
+    w = Workload("nanc", 0, 0, 130, 70, 40, 1.0, 0.0, seed=3)
+    A, B, C = workloads.make_inputs(w)
+    C[:] = np.nan
+    st, got = run_gpu(env, w, A, B, C)
+    assert st == 0
+    assert np.isfinite(c_items(got, w)).all()
+    check_against_oracle(w, A, B, C, got)
+
+
+@pytest.mark.parametrize("alpha,K", [(0.0, 50), (1.0, 0), (0.0, 0)])
+@pytest.mark.parametrize("beta", [0.0, 1.0, -2.5])
+def test_alpha_zero_or_k_zero_scales_c(env, alpha, K, beta):
+    w = Workload("scale", 0, 0, 77, 33, K, alpha, beta, seed=5, batch=3, ldc=40)
+    A, B, C = workloads.make_inputs(w)
+    if alpha == 0.0 and K:
+        A[:] = np.nan  # A and B are not read
+    st, got = run_gpu(env, w, A, B, C)
+    assert st == 0
+    want = c_items(C, w) * np.float32(beta)
+    if beta == 0.0:
+        want = np.zeros_like(want)
+    assert np.array_equal(c_items(got, w), want)
+    check_untouched(w, C, got)
+
+
+@pytest.mark.parametrize("dims", [(0, 5, 5, 1), (5, 0, 5, 1), (5, 5, 5, 0)])
+def test_empty_problems_touch_nothing(env, dims):
+    M, N, K, batch = dims
+    w = Workload("empty", 0, 0, M, N, K, 1.0, 0.0, seed=1, batch=batch, lda=8, ldb=8, ldc=8,
+                 stride_a=64, stride_b=64, stride_c=64)
+    A = np.ones(64, np.float32)
+    B = np.ones(64, np.float32)
+    C = np.arange(64, dtype=np.float32)
+    st, got = run_gpu(env, w, A, B, C)
+    assert st == 0
+    assert np.array_equal(got, C)
+
+
+def test_broadcast_and_strided_batches(env):
+    """strideA = 0 (one A shared by all items), B and C items with gaps."""
+    w = Workload("bcast", 0, 1, 200, 136, 96, 1.0, 0.5, seed=9, batch=5,
+                 stride_a=0, stride_b=136 * 96 + 12, stride_c=200 * 136 + 36)
+    A, B, C = workloads.make_inputs(w)
+    for variant in (-1, 0, 1, 2, 3):
+        st, got = run_gpu(env, w, A, B, C, variant=variant)
+        assert st == 0
+        check_against_oracle(w, A, B, C, got)
+        check_untouched(w, C, got)
+
+
+def test_unaligned_pointers_use_the_scalar_variant(env):
+    """C offset by one float and odd leading dimensions: auto-dispatch must
+    still give correct results (the 1-float-load variant)."""
+    w = Workload("odd", 1, 1, 101, 67, 45, -1.0, 2.0, seed=11, lda=103, ldb=47, ldc=69)
+    A, B, C = workloads.make_inputs(w)
+    st, got = run_gpu(env, w, A, B, C, c_offset=1)
+    assert st == 0
+    check_against_oracle(w, A, B, C, got)
+    check_untouched(w, C, got)
+
+
+def test_deterministic(env):
+    w = Workload("det", 0, 0, 1000, 1000, 1000, 1.0, 0.5, seed=13)
+    A, B, C = workloads.make_inputs(w)
+    _, g1 = run_gpu(env, w, A, B, C)
+    _, g2 = run_gpu(env, w, A, B, C)
+    assert np.array_equal(g1.view(np.uint32), g2.view(np.uint32))
+
+
+def test_matmul_tensor_wrapper(env):
+    torch, pg = env
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device="cpu").manual_seed(0)
+    A = torch.randn(3, 70, 50, generator=g)
+    B = torch.randn(3, 60, 50, generator=g)
+    C = torch.randn(3, 70, 60, generator=g)
+    dC = C.to(dev)
+    pg.matmul(A.to(dev), B.to(dev), dC, alpha=2.0, beta=-1.0, transB=True)
+    torch.cuda.synchronize(dev)
+    want = 2.0 * (A.double() @ B.double().transpose(1, 2)) - C.double()
+    S = 2.0 * (A.double().abs() @ B.double().abs().transpose(1, 2)) + C.double().abs()
+    err = (dC.cpu().double() - want).abs()
+    assert bool((err <= 2e-6 * 50 * S).all())
