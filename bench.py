@@ -73,7 +73,6 @@ def cpu_baseline(w, A, B, C, got_c, target_s: float):
     probe_rows = min(w.M, max(threads, 16))
     t_probe, _, _ = run(probe_rows)
     rows = int(min(w.M, max(probe_rows, probe_rows * target_s / max(t_probe, 1e-6))))
-    rows = max(1, rows - rows % threads) if rows > threads else rows
     t, ref, S = run(rows)
     gflops = rows * per_row_flops / t / 1e9
     # the sampled rows double as a parity check of the first timed launch
@@ -96,6 +95,29 @@ def cpu_baseline(w, A, B, C, got_c, target_s: float):
     }
 
 
+def copy_reference(torch, dev, args) -> int:
+    """Time dst.copy_(src) of a known size: the kernel whose FETCH_SIZE and
+    WRITE_SIZE readings calibrate the counters against true bytes."""
+    n = args.copy_mib * (1 << 20) // 4
+    src = torch.rand(n, device=dev)
+    dst = torch.empty_like(src)
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(max(1, args.warmup)):
+        dst.copy_(src)
+    torch.cuda.synchronize(dev)
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(args.steps):
+        dst.copy_(src)
+    t1.record(stream)
+    torch.cuda.synchronize(dev)
+    ms = t0.elapsed_time(t1) / args.steps
+    print(json.dumps({"copy_bytes_read": 4 * n, "copy_bytes_written": 4 * n,
+                      "ms_per_copy": round(ms, 5),
+                      "gbs_read_plus_write": round(8 * n / (ms * 1e-3) / 1e9, 1)}), flush=True)
+    return 0
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -107,6 +129,9 @@ def main(argv=None) -> int:
                     help="approximate CPU time for the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the oracle leg (profiling runs)")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="instead of SGEMM, time a plain device copy of this many MiB "
+                         "(reference kernel for scaling HBM byte counters)")
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
@@ -122,10 +147,12 @@ def main(argv=None) -> int:
     from precision_gemm_amd import measure
     import workloads
 
-    w = workloads.BY_NAME[args.config]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     props = torch.cuda.get_device_properties(dev)
+    if args.copy_mib:
+        return copy_reference(torch, dev, args)
+    w = workloads.BY_NAME[args.config]
     A, B, C = workloads.make_inputs(w)
     dA, dB, dC = (torch.from_numpy(x).to(dev) for x in (A, B, C))
     stream = torch.cuda.current_stream(dev)

@@ -33,7 +33,9 @@ _lib = None
 
 
 def library_path() -> str:
-    return os.path.join(_HERE, "libsgemm.so")
+    """The in-tree library; SGEMM_LIBRARY may name another build of the same
+    source (used when comparing tuning builds side by side)."""
+    return os.environ.get("SGEMM_LIBRARY") or os.path.join(_HERE, "libsgemm.so")
 
 
 class SgemmError(RuntimeError):

@@ -22,8 +22,8 @@
 //     nothing extra: only the address map and the LDS layout change.
 //       - k-contiguous operand (A with transA=0, B with transB=1): LDS rows
 //         of BK floats, one per output row/column, with the 16-byte column
-//         XOR-swizzled by row so that 128-bit reads of eight consecutive
-//         rows hit distinct banks;
+//         XOR-swizzled by row so that 128-bit reads of consecutive rows
+//         spread over all 64 LDS banks;
 //       - outer-contiguous operand (A with transA=1, B with transB=0): LDS
 //         rows of BM (or BN) floats, one per k, read one float per lane.
 //   * The k index is permuted inside every group of 8: MFMA step j of a
@@ -45,6 +45,7 @@
 #include <hip/hip_runtime.h>
 
 #include <atomic>
+#include <type_traits>
 #include <stdint.h>
 
 #include "sgemm.h"
@@ -110,7 +111,11 @@ struct Operand {
     static constexpr int SLOTS = BO * BK / (4 * NT);     // 16-byte chunks per thread
     static constexpr int EPS = VEC == 4 ? 1 : 4;         // byte offsets kept per slot
     static constexpr int NOFF = SLOTS * EPS;
-    static constexpr int SWZ_ROWS = BK >= 32 ? 1 : 32 / BK; // rows sharing one 32-bank sweep
+    // gfx950 serves a 128-bit LDS read from 64 four-byte banks: with k-contiguous
+    // rows of BK floats, 64/BK consecutive rows share one sweep of the banks, so
+    // the 16-byte chunk index is XORed with (row / (64/BK)) to spread the rows
+    // of one read over all banks (measured conflict-free with rocprofv3).
+    static constexpr int SWZ_ROWS = BK >= 64 ? 1 : 64 / BK;
     static_assert(BO * BK % (4 * NT) == 0 && SLOTS >= 1, "tile does not split evenly");
     static_assert(BK % 8 == 0, "BK must be a multiple of 8");
     static_assert(VEC == 4 || VEC == 1, "VEC");
@@ -184,18 +189,21 @@ struct Operand {
     }
 
     // MFMA operands of k-group q (8 k values) for the 32-row slab at outer
-    // offset w (inside the tile): v[j] feeds MFMA step j of the group.
-    __device__ __forceinline__ static f32x4 frag(const float *lds, int w, int q, int lane)
+    // offset w (inside the tile): v[j] feeds MFMA step j of the group. Kept as
+    // four scalars so every LDS read result feeds its MFMA directly.
+    __device__ __forceinline__ static void frag(const float *lds, int w, int q, int lane,
+                                                float (&v)[4])
     {
         const int o = w + (lane & 31), g = lane >> 5;
         if (KC) {
-            return *reinterpret_cast<const f32x4 *>(lds + lds_index(o, 2 * q + g));
+            const f32x4 x = *reinterpret_cast<const f32x4 *>(lds + lds_index(o, 2 * q + g));
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                v[j] = x[j];
         } else {
-            f32x4 v;
 #pragma unroll
             for (int j = 0; j < 4; ++j)
                 v[j] = lds[(8 * q + 4 * g + j) * ROW + o];
-            return v;
         }
     }
 };
@@ -271,13 +279,36 @@ sgemm_mfma_kernel(Params p)
     f32x4 ra[OpA::SLOTS], rb[OpB::SLOTS];
     const int nsteps = (p.K + BK - 1) / BK;
 
+    // EVEN_K: every K-step is full and loads carry no k mask. Otherwise each
+    // load also checks its k index against K (a compare and an OR per load,
+    // with no branch), which zero-fills the masked tail of the last step.
     auto load_step = [&](int s) {
-        if (!EVEN_K && s == nsteps - 1) {
-            opa.template load<true>(tid, s * BK, ra);
-            opb.template load<true>(tid, s * BK, rb);
-        } else {
-            opa.template load<false>(tid, s * BK, ra);
-            opb.template load<false>(tid, s * BK, rb);
+        opa.template load<!EVEN_K>(tid, s * BK, ra);
+        opb.template load<!EVEN_K>(tid, s * BK, rb);
+    };
+
+    constexpr int NQ = BK / 8;      // groups of 8 k per K-step
+    constexpr int LATE = TM * TN;   // MFMAs of the last group issued after the barrier
+    static_assert(NQ >= 2, "the fragment pipeline needs at least two k-groups per step");
+
+    auto read_group = [&](const float *stage, int q, float (&fa)[TM][4], float (&fb)[TN][4]) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+            OpA::frag(stage, wm0 + 32 * i, q, lane, fa[i]);
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+            OpB::frag(stage + OpA::STAGE, wn0 + 32 * j, q, lane, fb[j]);
+    };
+    // MFMA steps [first, last) of one k-group, step-major so that consecutive
+    // MFMAs update different accumulators.
+    auto mfma_group = [&](const float (&fa)[TM][4], const float (&fb)[TN][4], int first, int last) {
+#pragma unroll
+        for (int t = 0; t < 4 * TM * TN; ++t) {
+            if (t < first || t >= last)
+                continue;
+            const int kk = t / (TM * TN), i = (t / TN) % TM, j = t % TN;
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[i][kk], fb[j][kk], acc[i][j],
+                                                              0, 0, 0);
         }
     };
 
@@ -288,35 +319,53 @@ sgemm_mfma_kernel(Params p)
         load_step(1);
     __syncthreads();
 
+    // Software pipeline over K-steps. Group 0 of a stage is read right after
+    // the barrier that publishes it, while the previous step's last MFMAs are
+    // still being issued; the other groups are read while group 0's MFMAs run.
+    // The next stage's LDS writes and the global loads two steps ahead go
+    // between MFMA groups. One barrier per step.
+    float fa[NQ][TM][4], fb[NQ][TN][4];
+    read_group(lds, 0, fa[0], fb[0]);
     for (int s = 0; s < nsteps; ++s) {
-        const float *la = lds + (s & 1) * STAGE;
-        const float *lb = la + OpA::STAGE;
+        const float *cur = lds + (s & 1) * STAGE;
+        float *nxt = lds + ((s + 1) & 1) * STAGE;
 #pragma unroll
-        for (int q = 0; q < BK / 8; ++q) {
-            f32x4 fa[TM], fb[TN];
+        for (int q = 1; q < NQ; ++q)
+            read_group(cur, q, fa[q], fb[q]);
+        mfma_group(fa[0], fb[0], 0, 4 * TM * TN);
+        // The stage written here is idle this step. On the last two steps the
+        // writes and loads are of no use but harmless (loads past K read zero
+        // through the buffer range); keeping them unconditional keeps the loop
+        // body one block that the scheduler can interleave.
+        OpA::store(nxt, tid, ra);
+        OpB::store(nxt + OpA::STAGE, tid, rb);
+        load_step(s + 2);
 #pragma unroll
-            for (int i = 0; i < TM; ++i)
-                fa[i] = OpA::frag(la, wm0 + 32 * i, q, lane);
+        for (int q = 1; q < NQ - 1; ++q)
+            mfma_group(fa[q], fb[q], 0, 4 * TM * TN);
+        mfma_group(fa[NQ - 1], fb[NQ - 1], 0, 4 * TM * TN - LATE);
+        // Order: this stage's remaining fragment reads, then MFMAs alternating
+        // with the next stage's LDS writes and the global loads.
+        __builtin_amdgcn_sched_group_barrier(0x100, 4 * (TM + TN) * (NQ - 1), 0);
 #pragma unroll
-            for (int j = 0; j < TN; ++j)
-                fb[j] = OpB::frag(lb, wn0 + 32 * j, q, lane);
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-                for (int i = 0; i < TM; ++i)
-#pragma unroll
-                    for (int j = 0; j < TN; ++j)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[i][kk], fb[j][kk],
-                                                                          acc[i][j], 0, 0, 0);
+        for (int w = 0; w < OpA::SLOTS + OpB::SLOTS; ++w) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0); // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x200, 1, 0); // LDS write
         }
-        if (s + 1 < nsteps) {
-            float *na = lds + ((s + 1) & 1) * STAGE;
-            OpA::store(na, tid, ra);
-            OpB::store(na + OpA::STAGE, tid, rb);
-            if (s + 2 < nsteps)
-                load_step(s + 2);
+#pragma unroll
+        for (int w = 0; w < (OpA::SLOTS + OpB::SLOTS) * OpA::EPS; ++w) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0); // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0); // global load
         }
+        __builtin_amdgcn_sched_barrier(0);
         __syncthreads();
+        __builtin_amdgcn_sched_barrier(0);
+        // (On the last step this reads the idle stage; the values are unused.)
+        read_group(nxt, 0, fa[0], fb[0]);
+        mfma_group(fa[NQ - 1], fb[NQ - 1], 4 * TM * TN - LATE, 4 * TM * TN);
+        // Issue the reads first so their latency runs under the late MFMAs.
+        __builtin_amdgcn_sched_group_barrier(0x100, 4 * (TM + TN), 0); // LDS reads
+        __builtin_amdgcn_sched_group_barrier(0x008, LATE, 0);          // MFMAs
     }
 
     // Epilogue: C = alpha * acc + beta * C, lanes outside M x N dropped.
@@ -327,25 +376,38 @@ sgemm_mfma_kernel(Params p)
     const __amdgpu_buffer_rsrc_t rc =
         make_rsrc(Cb + cbase, (long long)(p.M - 1) * p.ldc + p.N - cbase);
     const int g = lane >> 5;
+    auto epilogue = [&](auto with_beta) {
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
+        for (int i = 0; i < TM; ++i) {
 #pragma unroll
-        for (int j = 0; j < TN; ++j) {
-            const int col = wn0 + 32 * j + (lane & 31);
-            const bool col_ok = n0 + col < p.N;
+            for (int j = 0; j < TN; ++j) {
+                const int col = wn0 + 32 * j + (lane & 31);
+                const bool col_ok = n0 + col < p.N;
+                uint32_t off[16];
+                float c[16];
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int row = wm0 + 32 * i + 8 * (v >> 2) + 4 * g + (v & 3);
-                const uint32_t off = (col_ok && m0 + row < p.M)
-                                         ? (uint32_t)(((long long)row * p.ldc + col) * 4)
-                                         : kOOB;
-                float out = p.alpha * acc[i][j][v];
-                if (p.beta != 0.0f)
-                    out += p.beta * load1(rc, off);
-                store1(rc, off, out);
+                for (int v = 0; v < 16; ++v) {
+                    const int row = wm0 + 32 * i + 8 * (v >> 2) + 4 * g + (v & 3);
+                    off[v] = (col_ok && m0 + row < p.M)
+                                 ? (uint32_t)(((long long)row * p.ldc + col) * 4)
+                                 : kOOB;
+                    if (with_beta)
+                        c[v] = load1(rc, off[v]);
+                }
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    float out = p.alpha * acc[i][j][v];
+                    if (with_beta)
+                        out += p.beta * c[v];
+                    store1(rc, off[v], out);
+                }
             }
         }
-    }
+    };
+    if (p.beta != 0.0f)
+        epilogue(std::true_type{});
+    else
+        epilogue(std::false_type{});
 }
 
 // C = beta * C over the M x N window of every batch item (alpha == 0 or K == 0).
