@@ -7,8 +7,8 @@ one kernel at a time" benchmarks) with its operands already resident in HBM.
 W untimed warm-up steps run first, then exactly K steps are timed between two
 device synchronisations with HIP events recorded on the stream the kernels
 run on (torch's current stream, which is the one passed to the library).
-Each timed step is also bracketed by its own event pair, giving the average
-duration of one kernel launch for the roofline figure.
+Every step is one kernel launch, so the timed region over K is also the
+average launch duration used for the roofline figure.
 
 Prints one JSON line. ``value`` is GFLOP/s (2*M*N*K per GEMM over the timed
 wall time). ``roofline`` reports the same kernel against the FP32-MFMA peak;
@@ -140,7 +140,6 @@ def main(argv=None) -> int:
               file=sys.stderr)
         return 2
 
-    import numpy as np
     import torch
 
     import precision_gemm_amd as pg
@@ -171,22 +170,22 @@ def main(argv=None) -> int:
         step()
     torch.cuda.synchronize(dev)
 
+    # Timed region: K launches back to back between two synchronisations,
+    # with one event pair around the whole region (per-launch events would put
+    # gaps between launches). Each step is exactly one kernel launch, so the
+    # region time over K is the average launch duration the roofline uses.
     K = args.steps
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(K)]
     region0, region1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize(dev)
     region0.record(stream)
-    for s in range(K):
-        ev[s][0].record(stream)
+    for _ in range(K):
         step()
-        ev[s][1].record(stream)
     region1.record(stream)
     torch.cuda.synchronize(dev)
 
     total_ms = region0.elapsed_time(region1)
-    per_launch_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
     ms_per_step = total_ms / K
+    per_launch_ms = ms_per_step
     flops = w.flops()
     value = flops / (ms_per_step * 1e-3) / 1e9
 

@@ -91,7 +91,9 @@ enum sgemm_variant {
     SGEMM_VARIANT_M128x128 = 1, /* 128 x 128 tile, 4 waves, 4-float loads */
     SGEMM_VARIANT_S64x64 = 2,   /*  64 x  64 tile, 4 waves, 4-float loads */
     SGEMM_VARIANT_S64x64_V1 = 3,/*  64 x  64 tile, 4 waves, 1-float loads (any alignment) */
-    SGEMM_VARIANT_COUNT = 4
+    SGEMM_VARIANT_T64x64 = 4,   /*  64 x  64 tile, 4 waves each on every 4th K-step,
+                                    direct-to-LDS streaming (few tiles, deep K) */
+    SGEMM_VARIANT_COUNT = 5
 };
 
 /*

@@ -410,6 +410,253 @@ sgemm_mfma_kernel(Params p)
         epilogue(std::false_type{});
 }
 
+// ---------------------------------------------------------------------------
+// Streaming kernel for few, deep tiles (a skinny N, or a grid too small to give
+// every CU a large tile): a 64 x 64 tile per workgroup whose four waves each
+// own every fourth K-step (wave w takes steps w, w+4, ...) and accumulate the
+// whole tile over their steps. Every wave fills its own ring of STAGES LDS
+// buffers with direct-to-LDS 16-byte buffer loads (buffer_load_dwordx4 ... lds:
+// lane i of an instruction writes the i-th 16 bytes of a 1 KiB block, an
+// out-of-range lane writes zeros) and reads back only what it loaded itself,
+// so the K loop needs no barrier: a wave waits on its own vmcnt only. Loads run
+// STAGES-1 steps ahead, which keeps enough bytes in flight per CU to stream A
+// at HBM rate. At the end the four partial tiles are summed through LDS in a
+// fixed order (deterministic) and the alpha/beta epilogue is applied.
+// ---------------------------------------------------------------------------
+template <bool KC, int BO, int BK>
+struct DmaOperand {
+    static constexpr int FLOATS = BO * BK;         // one K-step tile
+    static constexpr int NINST = FLOATS * 4 / 1024; // 1 KiB blocks, one load instruction each
+    static constexpr int C4 = KC ? BK / 4 : BO / 4; // 16-byte chunks per stored row of the tile
+    static constexpr int SWZ_ROWS = BK >= 64 ? 1 : 64 / BK;
+    static_assert(FLOATS * 4 % 1024 == 0, "tile must be whole 1 KiB blocks");
+
+    const float *X;
+    long long ld, total;
+    int O, K, o0;
+    uint32_t off[NINST]; // this lane's chunk in block b, relative to the step's window
+
+    __device__ __forceinline__ static int swz(int r) { return (r / SWZ_ROWS) % (BK / 4); }
+
+    // Block b, lane: LDS chunk position f = 64 b + lane. KC: row f / C4 holds
+    // logical chunk (f % C4) ^ swz(row); otherwise row f / C4 (a k) holds
+    // chunk f % C4 (four outer indices).
+    __device__ __forceinline__ void chunk(int b, int lane, int &r, int &c) const
+    {
+        const int f = 64 * b + lane;
+        r = f / C4;
+        c = KC ? (f % C4) ^ swz(r) : f % C4;
+    }
+
+    __device__ __forceinline__ void init(int lane)
+    {
+#pragma unroll
+        for (int b = 0; b < NINST; ++b) {
+            int r, c;
+            chunk(b, lane, r, c);
+            const bool ok = KC ? (o0 + r < O) : (o0 + 4 * c < O);
+            off[b] = ok ? (uint32_t)(((long long)r * ld + 4 * c) * 4) : kOOB;
+        }
+    }
+
+    template <bool TAIL>
+    __device__ __forceinline__ void issue(float *tile, int lane, int k0) const
+    {
+        const long long base = KC ? (long long)o0 * ld + k0 : (long long)k0 * ld + o0;
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(X + base, total - base);
+#pragma unroll
+        for (int b = 0; b < NINST; ++b) {
+            uint32_t o = off[b];
+            if (TAIL) {
+                int r, c;
+                chunk(b, lane, r, c);
+                if (!(KC ? (k0 + 4 * c < K) : (k0 + r < K)))
+                    o |= kOOB;
+            }
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rs, (__attribute__((address_space(3))) void *)(tile + 256 * b), 16, o, 0, 0, 0);
+        }
+    }
+
+    // Same operand layout contract as Operand::frag (k permuted within groups of 8).
+    __device__ __forceinline__ static void frag(const float *tile, int w, int q, int lane,
+                                                float (&v)[4])
+    {
+        const int o = w + (lane & 31), g = lane >> 5;
+        if (KC) {
+            const int c = 2 * q + g;
+            const f32x4 x =
+                *reinterpret_cast<const f32x4 *>(tile + o * BK + 4 * (c ^ swz(o)));
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                v[j] = x[j];
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                v[j] = tile[(8 * q + 4 * g + j) * BO + o];
+        }
+    }
+};
+
+// s_waitcnt immediate that waits for vmcnt <= n only (gfx9 encoding: vmcnt in
+// bits 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at their maxima).
+constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
+template <int STAGES, bool A_KC, bool B_KC, bool EVEN_K>
+__global__ void __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1)))
+sgemm_stream_kernel(Params p)
+{
+    constexpr int BM = 64, BN = 64, BK = 16, WAVES = 4, TM = 2, TN = 2, NQ = BK / 8;
+    using OpA = DmaOperand<A_KC, BM, BK>;
+    using OpB = DmaOperand<B_KC, BN, BK>;
+    constexpr int STAGE = OpA::FLOATS + OpB::FLOATS;      // floats per ring slot
+    constexpr int NI = OpA::NINST + OpB::NINST;           // load instructions per step
+    constexpr int PITCH = BN + 4;                         // partial-tile row pitch
+    constexpr int RING = WAVES * STAGES * STAGE;
+    constexpr int PART = WAVES * BM * PITCH;
+    static_assert((STAGES - 2) * NI <= 63, "vmcnt holds at most 63");
+    __shared__ __attribute__((aligned(16))) float lds[RING > PART ? RING : PART];
+
+    int b, tile_m, tile_n;
+    tile_of(p, b, tile_m, tile_n);
+    const int m0 = tile_m * BM, n0 = tile_n * BN;
+    // The wave index is uniform across the wave; saying so keeps the LDS
+    // destination of the direct loads (M0) a scalar.
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+
+    OpA opa;
+    opa.X = p.A + b * p.sA;
+    opa.ld = p.lda;
+    opa.total = A_KC ? (long long)(p.M - 1) * p.lda + p.K : (long long)(p.K - 1) * p.lda + p.M;
+    opa.O = p.M;
+    opa.K = p.K;
+    opa.o0 = m0;
+    opa.init(lane);
+    OpB opb;
+    opb.X = p.B + b * p.sB;
+    opb.ld = p.ldb;
+    opb.total = B_KC ? (long long)(p.N - 1) * p.ldb + p.K : (long long)(p.K - 1) * p.ldb + p.N;
+    opb.O = p.N;
+    opb.K = p.K;
+    opb.o0 = n0;
+    opb.init(lane);
+
+    float *ring = lds + wave * STAGES * STAGE;
+    // My j-th step is K-step wave + 4 j. Steps past K load zeros (or unused
+    // in-range data) into slots that are never read, which keeps the number
+    // of outstanding loads, and so every vmcnt wait, a constant.
+    auto issue = [&](int j) {
+        const int k0 = (wave + WAVES * j) * BK;
+        float *slot = ring + (j % STAGES) * STAGE;
+        opa.template issue<!EVEN_K>(slot, lane, k0);
+        opb.template issue<!EVEN_K>(slot + OpA::FLOATS, lane, k0);
+    };
+    float fa[2][NQ][TM][4], fb[2][NQ][TN][4];
+    auto read = [&](int j, float (&xa)[NQ][TM][4], float (&xb)[NQ][TN][4]) {
+        const float *slot = ring + (j % STAGES) * STAGE;
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+                OpA::frag(slot, 32 * i, q, lane, xa[q][i]);
+#pragma unroll
+            for (int t = 0; t < TN; ++t)
+                OpB::frag(slot + OpA::FLOATS, 32 * t, q, lane, xb[q][t]);
+        }
+    };
+
+    f32x16 acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int t = 0; t < TN; ++t)
+            acc[i][t] = f32x16{};
+
+    const int nsteps = (p.K + BK - 1) / BK;
+    const int mine = wave < nsteps ? (nsteps - wave + WAVES - 1) / WAVES : 0;
+#pragma unroll
+    for (int j = 0; j < STAGES - 1; ++j)
+        issue(j);
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm((STAGES - 2) * NI));
+    read(0, fa[0], fb[0]);
+    for (int j = 0; j < mine; j += 2) {
+        // Two steps per trip so the register double buffer has static indices.
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            if (h == 1 && j + 1 >= mine)
+                break;
+            issue(j + h + STAGES - 1);
+            __builtin_amdgcn_s_waitcnt(waitcnt_vm((STAGES - 2) * NI));
+            read(j + h + 1, fa[h ^ 1], fb[h ^ 1]);
+#pragma unroll
+            for (int q = 0; q < NQ; ++q)
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+                    for (int i = 0; i < TM; ++i)
+#pragma unroll
+                        for (int t = 0; t < TN; ++t)
+                            acc[i][t] = __builtin_amdgcn_mfma_f32_32x32x2f32(
+                                fa[h][q][i][kk], fb[h][q][t][kk], acc[i][t], 0, 0, 0);
+        }
+    }
+
+    // Sum the four partial tiles in a fixed order and apply the epilogue.
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    float *part = lds + wave * BM * PITCH;
+    const int g = lane >> 5;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int t = 0; t < TN; ++t)
+#pragma unroll
+            for (int v = 0; v < 16; ++v)
+                part[(32 * i + 8 * (v >> 2) + 4 * g + (v & 3)) * PITCH + 32 * t + (lane & 31)] =
+                    acc[i][t][v];
+    __syncthreads();
+    const int row = 16 * wave + (lane >> 2), col0 = 16 * (lane & 3);
+    float sum[16];
+#pragma unroll
+    for (int c = 0; c < 16; c += 4) {
+        f32x4 x = *reinterpret_cast<const f32x4 *>(lds + row * PITCH + col0 + c);
+#pragma unroll
+        for (int w = 1; w < WAVES; ++w) {
+            const f32x4 y =
+                *reinterpret_cast<const f32x4 *>(lds + (w * BM + row) * PITCH + col0 + c);
+            x += y;
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            sum[c + e] = x[e];
+    }
+    float *Cb = p.C + b * p.sC;
+    const long long cbase = (long long)m0 * p.ldc + n0;
+    const __amdgpu_buffer_rsrc_t rc =
+        make_rsrc(Cb + cbase, (long long)(p.M - 1) * p.ldc + p.N - cbase);
+    const bool row_ok = m0 + row < p.M;
+    uint32_t off[16];
+#pragma unroll
+    for (int c = 0; c < 16; ++c)
+        off[c] = (row_ok && n0 + col0 + c < p.N)
+                     ? (uint32_t)(((long long)row * p.ldc + col0 + c) * 4)
+                     : kOOB;
+    if (p.beta != 0.0f) {
+        float cin[16];
+#pragma unroll
+        for (int c = 0; c < 16; ++c)
+            cin[c] = load1(rc, off[c]);
+#pragma unroll
+        for (int c = 0; c < 16; ++c)
+            store1(rc, off[c], p.alpha * sum[c] + p.beta * cin[c]);
+    } else {
+#pragma unroll
+        for (int c = 0; c < 16; ++c)
+            store1(rc, off[c], p.alpha * sum[c]);
+    }
+}
+
 // C = beta * C over the M x N window of every batch item (alpha == 0 or K == 0).
 __global__ void __launch_bounds__(256) sgemm_scale_kernel(float *C, int M, int N, int ldc,
                                                           long long sC, int batch, float beta)
@@ -452,11 +699,26 @@ constexpr VariantInfo make_variant()
 
 constexpr int kBK = 16;
 
+template <int STAGES>
+constexpr VariantInfo make_stream_variant()
+{
+    return VariantInfo{64, 64, 256, 4,
+                       {{{sgemm_stream_kernel<STAGES, true, false, false>,
+                          sgemm_stream_kernel<STAGES, true, false, true>},
+                         {sgemm_stream_kernel<STAGES, true, true, false>,
+                          sgemm_stream_kernel<STAGES, true, true, true>}},
+                        {{sgemm_stream_kernel<STAGES, false, false, false>,
+                          sgemm_stream_kernel<STAGES, false, false, true>},
+                         {sgemm_stream_kernel<STAGES, false, true, false>,
+                          sgemm_stream_kernel<STAGES, false, true, true>}}}};
+}
+
 const VariantInfo kVariants[SGEMM_VARIANT_COUNT] = {
     make_variant<256, 128, kBK, 2, 2, 2, 4>(), // SGEMM_VARIANT_L256x128
     make_variant<128, 128, kBK, 2, 2, 2, 4>(), // SGEMM_VARIANT_M128x128
     make_variant<64, 64, kBK, 2, 2, 4, 4>(),   // SGEMM_VARIANT_S64x64
     make_variant<64, 64, kBK, 2, 2, 4, 1>(),   // SGEMM_VARIANT_S64x64_V1
+    make_stream_variant<4>(),                  // SGEMM_VARIANT_T64x64
 };
 
 long long ceil_div(long long a, long long b) { return (a + b - 1) / b; }
@@ -532,10 +794,15 @@ extern "C" int sgemm_select_variant(int transA, int transB, int M, int N, int K,
     // tiles need two resident workgroups per CU to cover their barriers.
     const long long tiles_l = ceil_div(M, 256) * ceil_div(N, 128) * batch;
     const long long tiles_m = ceil_div(M, 128) * ceil_div(N, 128) * batch;
+    const long long tiles_s = ceil_div(M, 64) * ceil_div(N, 64) * batch;
     if (tiles_l >= 2LL * num_cus)
         return SGEMM_VARIANT_L256x128;
     if (tiles_m >= 2LL * num_cus)
         return SGEMM_VARIANT_M128x128;
+    // Few 64 x 64 tiles over a deep K: split each tile's K over four waves
+    // that stream their operands through their own LDS rings.
+    if (K >= 256 && tiles_s <= 2LL * num_cus)
+        return SGEMM_VARIANT_T64x64;
     return SGEMM_VARIANT_S64x64;
 }
 

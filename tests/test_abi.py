@@ -119,8 +119,9 @@ def test_select_variant(pg):
     # batched 64 x 512^2: 2 x 4 x 64 = 512 tiles
     assert sel(1, 0, 512, 512, 520, 64, True, 256) == pg.VARIANT_L256x128
     # 1024^3 is too small for the large tiles on 256 CUs
-    assert sel(0, 0, 1024, 1024, 1024, 1, True, 256) == pg.VARIANT_S64x64
+    assert sel(0, 0, 1024, 1024, 1024, 1, True, 256) == pg.VARIANT_T64x64
+    assert sel(0, 0, 1024, 1024, 128, 1, True, 256) == pg.VARIANT_S64x64
     assert sel(0, 0, 2048, 2048, 2048, 2, True, 256) == pg.VARIANT_M128x128
-    assert sel(0, 1, 16384, 64, 4096, 1, True, 256) == pg.VARIANT_S64x64
+    assert sel(0, 1, 16384, 64, 4096, 1, True, 256) == pg.VARIANT_T64x64
     assert sel(0, 0, 4092, 4092, 4092, 1, False, 256) == pg.VARIANT_S64x64_V1
     assert sel(3, 0, 4, 4, 4, 1, True, 256) == -1
