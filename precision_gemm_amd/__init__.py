@@ -18,7 +18,7 @@ __all__ = [
     "SgemmError", "sgemm", "sgemm_strided_batched", "sgemm_strided_batched_variant",
     "sgemm_status_string", "sgemm_select_variant", "matmul", "library_path",
     "VARIANT_AUTO", "VARIANT_L256x128", "VARIANT_M128x128", "VARIANT_S64x64",
-    "VARIANT_S64x64_V1", "VARIANT_T64x64", "VARIANT_NAMES",
+    "VARIANT_S64x64_V1", "VARIANT_T64x64", "VARIANT_L256x256", "VARIANT_NAMES",
 ]
 
 VARIANT_AUTO = -1
@@ -27,7 +27,9 @@ VARIANT_M128x128 = 1
 VARIANT_S64x64 = 2
 VARIANT_S64x64_V1 = 3
 VARIANT_T64x64 = 4
-VARIANT_NAMES = {0: "L256x128", 1: "M128x128", 2: "S64x64", 3: "S64x64_V1", 4: "T64x64"}
+VARIANT_L256x256 = 5
+VARIANT_NAMES = {0: "L256x128", 1: "M128x128", 2: "S64x64", 3: "S64x64_V1", 4: "T64x64",
+                 5: "L256x256"}
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _lib = None

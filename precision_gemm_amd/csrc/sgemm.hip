@@ -126,6 +126,16 @@ struct Operand {
     int O, K;         // outer extent and K of the product
     int o0;           // first outer index of this tile
     uint32_t off[NOFF];
+    // Window of the next K-step to load: its first element and first k. The
+    // buffer range of a window is the bytes left from its start to the end of
+    // the operand, capped at 2^31 - 1: while `big` is positive the window is
+    // capped, after that `rem` holds the exact bytes left (negative once past
+    // the end). Both advance with 32-bit scalar arithmetic only.
+    const float *wp;
+    int kn;
+    int32_t big;
+    int32_t rem;
+    int32_t step_bytes;
 
     __device__ __forceinline__ static int swz(int r) { return (r / SWZ_ROWS) % (BK / 4); }
 
@@ -149,20 +159,36 @@ struct Operand {
                 off[s * EPS + e] = ok ? (uint32_t)((elem + e) * 4) : kOOB;
             }
         }
+        const long long base = KC ? (long long)o0 * ld : (long long)o0;
+        wp = X + base;
+        kn = 0;
+        step_bytes = (int32_t)(KC ? 4LL * BK : 4LL * BK * ld);
+        const long long left = 4 * (total - base);
+        if (left > (long long)kMaxRange) {
+            const long long capped = (left - kMaxRange + step_bytes - 1) / step_bytes;
+            big = (int32_t)capped;
+            rem = (int32_t)(left - capped * step_bytes);
+        } else {
+            big = 0;
+            rem = (int32_t)left;
+        }
     }
 
-    // Issue the loads of the K-step starting at k0 into regs.
+    // Issue the loads of the next K-step into regs and advance the window.
+    // TAIL: also mask k >= K (needed only for a partial last step).
     template <bool TAIL>
-    __device__ __forceinline__ void load(int tid, int k0, f32x4 (&regs)[SLOTS]) const
+    __device__ __forceinline__ void load_next(int tid, f32x4 (&regs)[SLOTS])
     {
-        const long long base = KC ? (long long)o0 * ld + k0 : (long long)k0 * ld + o0;
-        const __amdgpu_buffer_rsrc_t rs = make_rsrc(X + base, total - base);
+        const bool capped = big > 0;
+        const uint32_t range = capped ? kMaxRange : (rem > 0 ? (uint32_t)rem : 0u);
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<float *>(wp), (short)0, (int)range, kRsrcWord3);
 #pragma unroll
         for (int s = 0; s < SLOTS; ++s) {
             const int f = tid + s * NT, r = f / C4, c4 = f % C4;
             if (VEC == 4) {
                 uint32_t o = off[s];
-                if (TAIL && !(KC ? (k0 + 4 * c4 < K) : (k0 + r < K)))
+                if (TAIL && !(KC ? (kn + 4 * c4 < K) : (kn + r < K)))
                     o |= kOOB;
                 regs[s] = load4(rs, o);
             } else {
@@ -170,13 +196,17 @@ struct Operand {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     uint32_t o = off[s * 4 + e];
-                    if (TAIL && !(KC ? (k0 + 4 * c4 + e < K) : (k0 + r < K)))
+                    if (TAIL && !(KC ? (kn + 4 * c4 + e < K) : (kn + r < K)))
                         o |= kOOB;
                     v[e] = load1(rs, o);
                 }
                 regs[s] = v;
             }
         }
+        wp += KC ? (long long)BK : (long long)BK * ld;
+        kn += BK;
+        big -= 1;
+        rem -= capped ? 0 : step_bytes;
     }
 
     __device__ __forceinline__ static void store(float *lds, int tid, const f32x4 (&regs)[SLOTS])
@@ -279,12 +309,14 @@ sgemm_mfma_kernel(Params p)
     f32x4 ra[OpA::SLOTS], rb[OpB::SLOTS];
     const int nsteps = (p.K + BK - 1) / BK;
 
-    // EVEN_K: every K-step is full and loads carry no k mask. Otherwise each
-    // load also checks its k index against K (a compare and an OR per load,
-    // with no branch), which zero-fills the masked tail of the last step.
-    auto load_step = [&](int s) {
-        opa.template load<!EVEN_K>(tid, s * BK, ra);
-        opb.template load<!EVEN_K>(tid, s * BK, rb);
+    // EVEN_K: every K-step is full and no load carries a k mask. Otherwise
+    // only the copies of the loop body that can load the partial last step
+    // (the prologue and the last iterations) compare k against K.
+    using Tail = std::bool_constant<!EVEN_K>;
+    using Full = std::false_type;
+    auto load = [&](auto tail) {
+        opa.template load_next<decltype(tail)::value>(tid, ra);
+        opb.template load_next<decltype(tail)::value>(tid, rb);
     };
 
     constexpr int NQ = BK / 8;      // groups of 8 k per K-step
@@ -312,34 +344,35 @@ sgemm_mfma_kernel(Params p)
         }
     };
 
-    load_step(0);
+    load(Tail{});
     OpA::store(lds, tid, ra);
     OpB::store(lds + OpA::STAGE, tid, rb);
-    if (nsteps > 1)
-        load_step(1);
+    load(Tail{});
     __syncthreads();
 
     // Software pipeline over K-steps. Group 0 of a stage is read right after
     // the barrier that publishes it, while the previous step's last MFMAs are
     // still being issued; the other groups are read while group 0's MFMAs run.
     // The next stage's LDS writes and the global loads two steps ahead go
-    // between MFMA groups. One barrier per step.
+    // between MFMA groups. One barrier per step. The step is written for a
+    // fixed stage parity, so every LDS address is a loop-invariant register
+    // plus an immediate offset and the loop body does no address arithmetic.
     float fa[NQ][TM][4], fb[NQ][TN][4];
     read_group(lds, 0, fa[0], fb[0]);
-    for (int s = 0; s < nsteps; ++s) {
-        const float *cur = lds + (s & 1) * STAGE;
-        float *nxt = lds + ((s + 1) & 1) * STAGE;
+    auto k_step = [&](auto parity, auto tail) {
+        constexpr int PAR = decltype(parity)::value;
+        const float *cur = lds + PAR * STAGE;
+        float *nxt = lds + (1 - PAR) * STAGE;
 #pragma unroll
         for (int q = 1; q < NQ; ++q)
             read_group(cur, q, fa[q], fb[q]);
         mfma_group(fa[0], fb[0], 0, 4 * TM * TN);
         // The stage written here is idle this step. On the last two steps the
-        // writes and loads are of no use but harmless (loads past K read zero
-        // through the buffer range); keeping them unconditional keeps the loop
-        // body one block that the scheduler can interleave.
+        // writes and loads are of no use but harmless (loads past the operand
+        // read zero through the buffer range).
         OpA::store(nxt, tid, ra);
         OpB::store(nxt + OpA::STAGE, tid, rb);
-        load_step(s + 2);
+        load(tail);
 #pragma unroll
         for (int q = 1; q < NQ - 1; ++q)
             mfma_group(fa[q], fb[q], 0, 4 * TM * TN);
@@ -366,6 +399,22 @@ sgemm_mfma_kernel(Params p)
         // Issue the reads first so their latency runs under the late MFMAs.
         __builtin_amdgcn_sched_group_barrier(0x100, 4 * (TM + TN), 0); // LDS reads
         __builtin_amdgcn_sched_group_barrier(0x008, LATE, 0);          // MFMAs
+    };
+    using P0 = std::integral_constant<int, 0>;
+    using P1 = std::integral_constant<int, 1>;
+    // Step s loads step s + 2; only a load of the partial last step needs the
+    // k mask, so steps before nsteps - 3 run unmasked, two per trip.
+    const int unmasked = EVEN_K ? nsteps : nsteps - 3;
+    int s = 0;
+    for (; s + 1 < unmasked; s += 2) {
+        k_step(P0{}, Full{});
+        k_step(P1{}, Full{});
+    }
+    // The pairs above end on an even step, so the rest starts at parity 0.
+    for (; s < nsteps; s += 2) {
+        k_step(P0{}, Tail{});
+        if (s + 1 < nsteps)
+            k_step(P1{}, Tail{});
     }
 
     // Epilogue: C = alpha * acc + beta * C, lanes outside M x N dropped.
@@ -719,6 +768,7 @@ const VariantInfo kVariants[SGEMM_VARIANT_COUNT] = {
     make_variant<64, 64, kBK, 2, 2, 4, 4>(),   // SGEMM_VARIANT_S64x64
     make_variant<64, 64, kBK, 2, 2, 4, 1>(),   // SGEMM_VARIANT_S64x64_V1
     make_stream_variant<4>(),                  // SGEMM_VARIANT_T64x64
+    make_variant<256, 256, kBK, 2, 4, 2, 4>(), // SGEMM_VARIANT_L256x256
 };
 
 long long ceil_div(long long a, long long b) { return (a + b - 1) / b; }

@@ -184,7 +184,7 @@ def vec4_possible(w):
            w.LDA % 4 == 0 and w.LDB % 4 == 0 and w.SA % 4 == 0 and w.SB % 4 == 0
 
 
-@pytest.mark.parametrize("variant", [0, 1, 2, 3, 4])
+@pytest.mark.parametrize("variant", [0, 1, 2, 3, 4, 5])
 def test_integer_sweep_bitwise(env, variant):
     """Every forced variant x transpose pair over ragged sizes, integer inputs:
     bitwise equality with the oracle."""
@@ -211,7 +211,7 @@ def test_integer_sweep_bitwise(env, variant):
     assert n_run > 20
 
 
-@pytest.mark.parametrize("variant", [0, 1, 2, 3, 4])
+@pytest.mark.parametrize("variant", [0, 1, 2, 3, 4, 5])
 def test_float_sweep_bound(env, variant):
     """Random fp32 inputs, several tiles plus ragged tails in every dimension,
     all transposes, padded leading dimensions, batches with gaps."""
@@ -278,7 +278,7 @@ def test_broadcast_and_strided_batches(env):
     w = Workload("bcast", 0, 1, 200, 136, 96, 1.0, 0.5, seed=9, batch=5,
                  stride_a=0, stride_b=136 * 96 + 12, stride_c=200 * 136 + 36)
     A, B, C = workloads.make_inputs(w)
-    for variant in (-1, 0, 1, 2, 3, 4):
+    for variant in (-1, 0, 1, 2, 3, 4, 5):
         st, got = run_gpu(env, w, A, B, C, variant=variant)
         assert st == 0
         check_against_oracle(w, A, B, C, got)
