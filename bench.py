@@ -4,7 +4,9 @@
 One step is one call of the library's ``sgemm`` on the workload (by default
 M = N = K = 4092, alpha = 1, beta = 0.5, the size "From 1% to 94% of cuBLAS,
 one kernel at a time" benchmarks) with its operands already resident in HBM.
-W untimed warm-up steps run first, then exactly K steps are timed between two
+W untimed warm-up steps run first (continued until at least --min-warmup-ms
+have passed, so the GPU clock has ramped up; the number actually run is
+reported as warmup_steps_run), then exactly K steps are timed between two
 device synchronisations with HIP events recorded on the stream the kernels
 run on (torch's current stream, which is the one passed to the library).
 Every step is one kernel launch, so the timed region over K is also the
@@ -125,6 +127,9 @@ def main(argv=None) -> int:
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="sgemm_4092", help="workload name (workloads.py)")
     ap.add_argument("--variant", type=int, default=-1, help="force a kernel variant (-1 auto)")
+    ap.add_argument("--min-warmup-ms", type=float, default=300.0,
+                    help="keep warming up until at least this much time has passed "
+                         "(the GPU clock takes tens of ms to ramp up under load)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate CPU time for the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true",
@@ -166,8 +171,16 @@ def main(argv=None) -> int:
     torch.cuda.synchronize(dev)
     first_out = dC.cpu().numpy() if not args.no_cpu_baseline else None
 
-    for _ in range(max(0, args.warmup - 1)):
+    # Untimed warm-up: the requested W steps, continued until the clock has
+    # had min_warmup_ms to ramp up (the first launches run well below the
+    # steady-state clock). The steps actually run are reported.
+    warm_run = 1
+    t_warm = time.perf_counter()
+    while warm_run < args.warmup or (time.perf_counter() - t_warm) * 1e3 < args.min_warmup_ms:
         step()
+        warm_run += 1
+        if warm_run % 8 == 0:
+            torch.cuda.synchronize(dev)
     torch.cuda.synchronize(dev)
 
     # Timed region: K launches back to back between two synchronisations,
@@ -204,6 +217,7 @@ def main(argv=None) -> int:
         "n_gpus": 1,
         "steps": K,
         "warmup": args.warmup,
+        "warmup_steps_run": warm_run,
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",

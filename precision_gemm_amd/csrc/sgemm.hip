@@ -484,6 +484,13 @@ struct DmaOperand {
     long long ld, total;
     int O, K, o0;
     uint32_t off[NINST]; // this lane's chunk in block b, relative to the step's window
+    // Window of this wave's next K-step (the waves of a workgroup take every
+    // WAVES-th step): first element and first k, and its buffer range kept as
+    // in Operand (`big` windows capped at 2^31 - 1, then `rem` exact bytes).
+    const float *wp;
+    int kn, kstep;
+    int32_t big, rem, step_bytes;
+    long long step_elems;
 
     __device__ __forceinline__ static int swz(int r) { return (r / SWZ_ROWS) % (BK / 4); }
 
@@ -497,7 +504,8 @@ struct DmaOperand {
         c = KC ? (f % C4) ^ swz(r) : f % C4;
     }
 
-    __device__ __forceinline__ void init(int lane)
+    // k0: first k of this wave's first step; kstride: k between its steps.
+    __device__ __forceinline__ void init(int lane, int k0, int kstride)
     {
 #pragma unroll
         for (int b = 0; b < NINST; ++b) {
@@ -506,25 +514,47 @@ struct DmaOperand {
             const bool ok = KC ? (o0 + r < O) : (o0 + 4 * c < O);
             off[b] = ok ? (uint32_t)(((long long)r * ld + 4 * c) * 4) : kOOB;
         }
+        const long long base = KC ? (long long)o0 * ld + k0 : (long long)k0 * ld + o0;
+        wp = X + base;
+        kn = k0;
+        kstep = kstride;
+        step_elems = KC ? (long long)kstride : (long long)kstride * ld;
+        step_bytes = (int32_t)(4 * step_elems);
+        const long long left = 4 * (total - base);
+        if (left > (long long)kMaxRange) {
+            const long long capped = (left - kMaxRange + step_bytes - 1) / step_bytes;
+            big = (int32_t)capped;
+            rem = (int32_t)(left - capped * step_bytes);
+        } else {
+            big = 0;
+            rem = left < 0 ? 0 : (int32_t)left;
+        }
     }
 
+    // Load this wave's next K-step into `tile` and advance the window.
     template <bool TAIL>
-    __device__ __forceinline__ void issue(float *tile, int lane, int k0) const
+    __device__ __forceinline__ void issue(float *tile, int lane)
     {
-        const long long base = KC ? (long long)o0 * ld + k0 : (long long)k0 * ld + o0;
-        const __amdgpu_buffer_rsrc_t rs = make_rsrc(X + base, total - base);
+        const bool capped = big > 0;
+        const uint32_t range = capped ? kMaxRange : (rem > 0 ? (uint32_t)rem : 0u);
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<float *>(wp), (short)0, (int)range, kRsrcWord3);
 #pragma unroll
         for (int b = 0; b < NINST; ++b) {
             uint32_t o = off[b];
             if (TAIL) {
                 int r, c;
                 chunk(b, lane, r, c);
-                if (!(KC ? (k0 + 4 * c < K) : (k0 + r < K)))
+                if (!(KC ? (kn + 4 * c < K) : (kn + r < K)))
                     o |= kOOB;
             }
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 rs, (__attribute__((address_space(3))) void *)(tile + 256 * b), 16, o, 0, 0, 0);
         }
+        wp += step_elems;
+        kn += kstep;
+        big -= 1;
+        rem -= capped ? 0 : step_bytes;
     }
 
     // Same operand layout contract as Operand::frag (k permuted within groups of 8).
@@ -581,7 +611,7 @@ sgemm_stream_kernel(Params p)
     opa.O = p.M;
     opa.K = p.K;
     opa.o0 = m0;
-    opa.init(lane);
+    opa.init(lane, wave * BK, WAVES * BK);
     OpB opb;
     opb.X = p.B + b * p.sB;
     opb.ld = p.ldb;
@@ -589,17 +619,16 @@ sgemm_stream_kernel(Params p)
     opb.O = p.N;
     opb.K = p.K;
     opb.o0 = n0;
-    opb.init(lane);
+    opb.init(lane, wave * BK, WAVES * BK);
 
     float *ring = lds + wave * STAGES * STAGE;
     // My j-th step is K-step wave + 4 j. Steps past K load zeros (or unused
     // in-range data) into slots that are never read, which keeps the number
     // of outstanding loads, and so every vmcnt wait, a constant.
     auto issue = [&](int j) {
-        const int k0 = (wave + WAVES * j) * BK;
         float *slot = ring + (j % STAGES) * STAGE;
-        opa.template issue<!EVEN_K>(slot, lane, k0);
-        opb.template issue<!EVEN_K>(slot + OpA::FLOATS, lane, k0);
+        opa.template issue<!EVEN_K>(slot, lane);
+        opb.template issue<!EVEN_K>(slot + OpA::FLOATS, lane);
     };
     float fa[2][NQ][TM][4], fb[2][NQ][TN][4];
     auto read = [&](int j, float (&xa)[NQ][TM][4], float (&xb)[NQ][TN][4]) {
@@ -840,20 +869,35 @@ extern "C" int sgemm_select_variant(int transA, int transB, int M, int N, int K,
         return SGEMM_VARIANT_S64x64_V1;
     if (num_cus < 1)
         num_cus = 1;
-    // Largest tile whose grid still gives every CU a workgroup; the large
-    // tiles need two resident workgroups per CU to cover their barriers.
-    const long long tiles_l = ceil_div(M, 256) * ceil_div(N, 128) * batch;
-    const long long tiles_m = ceil_div(M, 128) * ceil_div(N, 128) * batch;
-    const long long tiles_s = ceil_div(M, 64) * ceil_div(N, 64) * batch;
-    if (tiles_l >= 2LL * num_cus)
-        return SGEMM_VARIANT_L256x128;
-    if (tiles_m >= 2LL * num_cus)
-        return SGEMM_VARIANT_M128x128;
-    // Few 64 x 64 tiles over a deep K: split each tile's K over four waves
-    // that stream their operands through their own LDS rings.
-    if (K >= 256 && tiles_s <= 2LL * num_cus)
+    const long long cus = num_cus;
+    const long long tiles256 = ceil_div(M, 256) * ceil_div(N, 256) * batch;
+    // One skinny dimension over a deep K: stream the long operand through
+    // per-wave LDS rings, four waves splitting each 64 x 64 tile's K.
+    if ((M <= 64 || N <= 64) && K >= 512 && ceil_div(M, 64) * ceil_div(N, 64) * batch <= 2 * cus)
         return SGEMM_VARIANT_T64x64;
-    return SGEMM_VARIANT_S64x64;
+    // Exactly one wave of 256 x 256 tiles over a deep K: the eight-wave
+    // workgroup (two waves per SIMD in step) edges out two 256 x 128
+    // workgroups per CU.
+    if (K >= 2048 && tiles256 <= cus && 10 * tiles256 >= 9 * cus)
+        return SGEMM_VARIANT_L256x256;
+    // Otherwise the tile whose busiest CU finishes first: a CU receives
+    // ceil(tiles / CUs) tiles, each costing its area over the variant's
+    // relative efficiency (smaller tiles reuse each loaded byte less).
+    struct Choice { int variant, bm, bn, eff_pct; };
+    const Choice choices[] = {{SGEMM_VARIANT_L256x128, 256, 128, 100},
+                              {SGEMM_VARIANT_M128x128, 128, 128, 97},
+                              {SGEMM_VARIANT_S64x64, 64, 64, 92}};
+    int best = SGEMM_VARIANT_S64x64;
+    double best_cost = -1.0;
+    for (const Choice &c : choices) {
+        const long long tiles = ceil_div(M, c.bm) * ceil_div(N, c.bn) * batch;
+        const double cost = (double)ceil_div(tiles, cus) * c.bm * c.bn * 100.0 / c.eff_pct;
+        if (best_cost < 0 || cost < best_cost) {
+            best = c.variant;
+            best_cost = cost;
+        }
+    }
+    return best;
 }
 
 extern "C" int sgemm_strided_batched_variant(int transA, int transB, int M, int N, int K,

@@ -114,14 +114,23 @@ def test_status_strings(pg):
 
 def test_select_variant(pg):
     sel = pg.sgemm_select_variant
-    # 4092^3: 16 x 32 tiles of 256 x 128 = 512 >= 2 per CU on 256 CUs
-    assert sel(0, 0, 4092, 4092, 4092, 1, True, 256) == pg.VARIANT_L256x128
-    # batched 64 x 512^2: 2 x 4 x 64 = 512 tiles
+    # 4092^3: one wave of 16 x 16 tiles of 256 x 256 on 256 CUs
+    assert sel(0, 0, 4092, 4092, 4092, 1, True, 256) == pg.VARIANT_L256x256
+    # batched 64 x 512^2: 512 tiles of 256 x 128 = two per CU
     assert sel(1, 0, 512, 512, 520, 64, True, 256) == pg.VARIANT_L256x128
-    # 1024^3 is too small for the large tiles on 256 CUs
-    assert sel(0, 0, 1024, 1024, 1024, 1, True, 256) == pg.VARIANT_T64x64
-    assert sel(0, 0, 1024, 1024, 128, 1, True, 256) == pg.VARIANT_S64x64
-    assert sel(0, 0, 2048, 2048, 2048, 2, True, 256) == pg.VARIANT_M128x128
+    # 8192^3: eight 256 x 128 tiles per CU beat sixteen 128 x 128 ones
+    assert sel(0, 0, 8192, 8192, 8192, 1, True, 256) == pg.VARIANT_L256x128
+    # 2048^3 and 6144^3: 128 x 128 tiles spread evenly over the CUs
+    assert sel(0, 0, 2048, 2048, 2048, 1, True, 256) == pg.VARIANT_M128x128
+    assert sel(0, 0, 6144, 6144, 6144, 1, True, 256) == pg.VARIANT_M128x128
+    # 3072^3: 2304 tiles of 64 x 64 are nine per CU, 128 x 128 tiles are 2.25
+    assert sel(0, 0, 3072, 3072, 3072, 1, True, 256) == pg.VARIANT_S64x64
+    # 1024^3: 64 x 64 tiles, one per CU
+    assert sel(0, 0, 1024, 1024, 1024, 1, True, 256) == pg.VARIANT_S64x64
+    # skinny shapes stream
     assert sel(0, 1, 16384, 64, 4096, 1, True, 256) == pg.VARIANT_T64x64
+    assert sel(0, 0, 64, 8192, 8192, 1, True, 256) == pg.VARIANT_T64x64
+    assert sel(0, 1, 16384, 64, 128, 1, True, 256) != pg.VARIANT_T64x64
+    # no 4-float loads: the 1-float variant
     assert sel(0, 0, 4092, 4092, 4092, 1, False, 256) == pg.VARIANT_S64x64_V1
     assert sel(3, 0, 4, 4, 4, 1, True, 256) == -1
