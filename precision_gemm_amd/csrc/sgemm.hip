@@ -581,11 +581,13 @@ struct DmaOperand {
 // bits 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at their maxima).
 constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
-template <int STAGES, bool A_KC, bool B_KC, bool EVEN_K>
-__global__ void __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1)))
+template <int WAVES, int STAGES, bool A_KC, bool B_KC, bool EVEN_K>
+__global__ void
+__attribute__((amdgpu_flat_work_group_size(64 * WAVES, 64 * WAVES), amdgpu_waves_per_eu(1)))
 sgemm_stream_kernel(Params p)
 {
-    constexpr int BM = 64, BN = 64, BK = 16, WAVES = 4, TM = 2, TN = 2, NQ = BK / 8;
+    constexpr int BM = 64, BN = 64, BK = 16, TM = 2, TN = 2, NQ = BK / 8;
+    constexpr int CPT = BM * BN / (64 * WAVES); // epilogue columns per thread
     using OpA = DmaOperand<A_KC, BM, BK>;
     using OpB = DmaOperand<B_KC, BN, BK>;
     constexpr int STAGE = OpA::FLOATS + OpB::FLOATS;      // floats per ring slot
@@ -594,6 +596,7 @@ sgemm_stream_kernel(Params p)
     constexpr int RING = WAVES * STAGES * STAGE;
     constexpr int PART = WAVES * BM * PITCH;
     static_assert((STAGES - 2) * NI <= 63, "vmcnt holds at most 63");
+    static_assert(CPT % 4 == 0 && BN % CPT == 0, "epilogue split");
     __shared__ __attribute__((aligned(16))) float lds[RING > PART ? RING : PART];
 
     int b, tile_m, tile_n;
@@ -694,10 +697,10 @@ sgemm_stream_kernel(Params p)
                 part[(32 * i + 8 * (v >> 2) + 4 * g + (v & 3)) * PITCH + 32 * t + (lane & 31)] =
                     acc[i][t][v];
     __syncthreads();
-    const int row = 16 * wave + (lane >> 2), col0 = 16 * (lane & 3);
-    float sum[16];
+    const int row = (int)threadIdx.x / (BN / CPT), col0 = ((int)threadIdx.x % (BN / CPT)) * CPT;
+    float sum[CPT];
 #pragma unroll
-    for (int c = 0; c < 16; c += 4) {
+    for (int c = 0; c < CPT; c += 4) {
         f32x4 x = *reinterpret_cast<const f32x4 *>(lds + row * PITCH + col0 + c);
 #pragma unroll
         for (int w = 1; w < WAVES; ++w) {
@@ -714,23 +717,23 @@ sgemm_stream_kernel(Params p)
     const __amdgpu_buffer_rsrc_t rc =
         make_rsrc(Cb + cbase, (long long)(p.M - 1) * p.ldc + p.N - cbase);
     const bool row_ok = m0 + row < p.M;
-    uint32_t off[16];
+    uint32_t off[CPT];
 #pragma unroll
-    for (int c = 0; c < 16; ++c)
+    for (int c = 0; c < CPT; ++c)
         off[c] = (row_ok && n0 + col0 + c < p.N)
                      ? (uint32_t)(((long long)row * p.ldc + col0 + c) * 4)
                      : kOOB;
     if (p.beta != 0.0f) {
-        float cin[16];
+        float cin[CPT];
 #pragma unroll
-        for (int c = 0; c < 16; ++c)
+        for (int c = 0; c < CPT; ++c)
             cin[c] = load1(rc, off[c]);
 #pragma unroll
-        for (int c = 0; c < 16; ++c)
+        for (int c = 0; c < CPT; ++c)
             store1(rc, off[c], p.alpha * sum[c] + p.beta * cin[c]);
     } else {
 #pragma unroll
-        for (int c = 0; c < 16; ++c)
+        for (int c = 0; c < CPT; ++c)
             store1(rc, off[c], p.alpha * sum[c]);
     }
 }
@@ -777,18 +780,18 @@ constexpr VariantInfo make_variant()
 
 constexpr int kBK = 16;
 
-template <int STAGES>
+template <int WAVES, int STAGES>
 constexpr VariantInfo make_stream_variant()
 {
-    return VariantInfo{64, 64, 256, 4,
-                       {{{sgemm_stream_kernel<STAGES, true, false, false>,
-                          sgemm_stream_kernel<STAGES, true, false, true>},
-                         {sgemm_stream_kernel<STAGES, true, true, false>,
-                          sgemm_stream_kernel<STAGES, true, true, true>}},
-                        {{sgemm_stream_kernel<STAGES, false, false, false>,
-                          sgemm_stream_kernel<STAGES, false, false, true>},
-                         {sgemm_stream_kernel<STAGES, false, true, false>,
-                          sgemm_stream_kernel<STAGES, false, true, true>}}}};
+    return VariantInfo{64, 64, 64 * WAVES, 4,
+                       {{{sgemm_stream_kernel<WAVES, STAGES, true, false, false>,
+                          sgemm_stream_kernel<WAVES, STAGES, true, false, true>},
+                         {sgemm_stream_kernel<WAVES, STAGES, true, true, false>,
+                          sgemm_stream_kernel<WAVES, STAGES, true, true, true>}},
+                        {{sgemm_stream_kernel<WAVES, STAGES, false, false, false>,
+                          sgemm_stream_kernel<WAVES, STAGES, false, false, true>},
+                         {sgemm_stream_kernel<WAVES, STAGES, false, true, false>,
+                          sgemm_stream_kernel<WAVES, STAGES, false, true, true>}}}};
 }
 
 const VariantInfo kVariants[SGEMM_VARIANT_COUNT] = {
@@ -796,7 +799,7 @@ const VariantInfo kVariants[SGEMM_VARIANT_COUNT] = {
     make_variant<128, 128, kBK, 2, 2, 2, 4>(), // SGEMM_VARIANT_M128x128
     make_variant<64, 64, kBK, 2, 2, 4, 4>(),   // SGEMM_VARIANT_S64x64
     make_variant<64, 64, kBK, 2, 2, 4, 1>(),   // SGEMM_VARIANT_S64x64_V1
-    make_stream_variant<4>(),                  // SGEMM_VARIANT_T64x64
+    make_stream_variant<4, 4>(),               // SGEMM_VARIANT_T64x64
     make_variant<256, 256, kBK, 2, 4, 2, 4>(), // SGEMM_VARIANT_L256x256
 };
 

@@ -318,3 +318,73 @@ def test_matmul_tensor_wrapper(env):
     S = 2.0 * (A.double().abs() @ B.double().abs().transpose(1, 2)) + C.double().abs()
     err = (dC.cpu().double() - want).abs()
     assert bool((err <= 2e-6 * 50 * S).all())
+
+
+# ------------------------------------------------------------------ extremes
+
+def test_batch_beyond_one_launch(env):
+    """More batch items than one launch's second grid axis holds (65535)."""
+    w = Workload("manybatch", 0, 1, 4, 8, 12, 1.0, -1.0, seed=21, dist="int3", batch=70000)
+    A, B, C = workloads.make_inputs(w)
+    st, got = run_gpu(env, w, A, B, C)
+    assert st == 0
+    for b0, b1 in ((0, 3), (65534, 65537), (69997, 70000)):
+        check_against_oracle(w, A, B, C, got, exact=True, batches=(b0, b1))
+
+
+@pytest.mark.parametrize("which", ["lda", "ldb", "ldc"])
+def test_leading_dimension_at_the_limit(env, which):
+    """Leading dimensions at 2^21 - 1, the largest the header allows."""
+    big = (1 << 21) - 1
+    kw = {which: big}
+    w = Workload("bigld", 0, 0, 5, 7, 9, 1.5, 0.5, seed=22, **kw)
+    A, B, C = workloads.make_inputs(w)
+    for variant in (-1, 3):  # the automatic choice (unaligned ld: 1-float loads) and forced
+        st, got = run_gpu(env, w, A, B, C, variant=variant)
+        assert st == 0
+        check_against_oracle(w, A, B, C, got)
+        check_untouched(w, C, got)
+
+
+def test_batch_offsets_beyond_2_pow_31_elements(env):
+    """A second batch item more than 2^31 floats (8 GiB) past the first: the
+    per-item offsets must be 64-bit. Only the two small windows are copied."""
+    torch, pg = env
+    dev = torch.device("cuda:0")
+    M, N, K = 20, 36, 44
+    stride = (1 << 31) + 64
+    rng = np.random.default_rng(23)
+    big = torch.empty(stride + M * K, dtype=torch.float32, device=dev)  # ~8 GiB
+    Bm = rng.integers(-3, 4, (2, K, N)).astype(np.float32)
+    Cm = rng.integers(-3, 4, (2, M, N)).astype(np.float32)
+    A0 = rng.integers(-3, 4, (M, K)).astype(np.float32)
+    A1 = rng.integers(-3, 4, (M, K)).astype(np.float32)
+    big[:M * K] = torch.from_numpy(A0.reshape(-1)).to(dev)
+    big[stride:stride + M * K] = torch.from_numpy(A1.reshape(-1)).to(dev)
+    dB = torch.from_numpy(Bm.reshape(-1)).to(dev)
+    dC = torch.from_numpy(Cm.reshape(-1)).to(dev)
+    log(f"[extreme] strideA={stride}")
+    for variant in (-1, 0, 2, 4):
+        dC.copy_(torch.from_numpy(Cm.reshape(-1)))
+        st = pg.sgemm_strided_batched_variant(0, 0, M, N, K, 1.0, big, K, dB, N, 2.0, dC, N, 2,
+                                              stride, K * N, M * N, variant, check=False)
+        torch.cuda.synchronize(dev)
+        assert st == 0, variant
+        got = dC.cpu().numpy().reshape(2, M, N)
+        for b, Ab in ((0, A0), (1, A1)):
+            want = Ab.astype(np.float64) @ Bm[b].astype(np.float64) + 2.0 * Cm[b]
+            assert np.array_equal(got[b], want.astype(np.float32)), (variant, b)
+    del big
+
+
+@pytest.mark.parametrize("shape", [(1, 1, 100000), (100000, 1, 64), (1, 100000, 64),
+                                   (3, 5, 65537), (2047, 3, 1025)])
+def test_degenerate_shapes(env, shape):
+    """Dot products, single columns and rows, deep ragged K."""
+    M, N, K = shape
+    for tA, tB in ((0, 0), (1, 1)):
+        w = Workload("degen", tA, tB, M, N, K, 1.0, 1.0, seed=M + N + K, dist="int3")
+        A, B, C = workloads.make_inputs(w)
+        st, got = run_gpu(env, w, A, B, C)
+        assert st == 0
+        check_against_oracle(w, A, B, C, got, exact=True)
