@@ -44,12 +44,17 @@
  *        ldc >= max(1, N)) and below 2^21 elements, which keeps every
  *        in-tile byte offset within 31 bits. A NULL pointer is an error only
  *        where it would be dereferenced. Nothing is launched on error.
+ *        The variant-forcing entry points return -18 for an unknown variant
+ *        or a 4-float variant the operands cannot use, whatever the
+ *        position of their `variant` argument.
  *    >0  a hipError_t raised when querying the device or launching.
  * sgemm_status_string() turns any status into a message.
  *
- * Alignment: none is required. When A, B and C are 16-byte aligned and
- * lda, ldb, ldc (and the batch strides) are multiples of 4, the kernels move
- * four floats per load; otherwise a one-float-per-load variant runs.
+ * Alignment: none is required. When A and B are 16-byte aligned, lda, ldb,
+ * strideA and strideB are multiples of 4, and so is each operand's extent
+ * along its stored rows (K for A with transA = 0 and for B with transB = 1,
+ * M or N otherwise), the kernels move four floats per load; otherwise a
+ * one-float-per-load variant runs.
  */
 #ifndef PRECISION_GEMM_AMD_SGEMM_H
 #define PRECISION_GEMM_AMD_SGEMM_H
@@ -121,6 +126,70 @@ int sgemm_strided_batched_variant(int transA, int transB, int M, int N, int K,
                                   int batch, long long strideA, long long strideB,
                                   long long strideC, int variant,
                                   sgemm_stream_t stream);
+
+/*
+ * Pointer-array batched form: batch item b computes
+ *     C_array[b] = alpha * op(A_array[b]) @ op(B_array[b]) + beta * C_array[b]
+ * with the row-major storage, leading dimensions and special cases above.
+ * This is the general batched layout next to the strided one of "Triton
+ * Optimization Reference (cuTile -> Triton)", section 3 (the batch index on
+ * the second grid axis): instead of base + b*stride, each batch item's
+ * operands come from an array.
+ *
+ * A_array, B_array and C_array are DEVICE arrays of `batch` DEVICE pointers,
+ * all owned by the caller; the kernels read the arrays, the host never does,
+ * so the arrays and their items must stay valid until the work completes.
+ * Items may repeat in A_array and B_array (shared operands); C items must not
+ * overlap each other or any A or B item. Status codes use the positions of
+ * this argument list (A_array -7, B_array -9, C_array -12, batch -14); NULL
+ * items are not detected. A_array and B_array may be NULL when alpha == 0 or
+ * K == 0, C_array when nothing is written.
+ *
+ * Alignment: none is required. When lda and ldb allow 4-float loads (see
+ * Alignment above), the kernels check each item's A and B pointers on the
+ * device and compute an item that is not 16-byte aligned with plain 4-byte
+ * loads, which is correct but much slower.
+ */
+int sgemm_batched(int transA, int transB, int M, int N, int K,
+                  float alpha, const float *const *A_array, int lda,
+                               const float *const *B_array, int ldb,
+                  float beta,        float *const *C_array, int ldc,
+                  int batch, sgemm_stream_t stream);
+
+/* sgemm_batched with the kernel variant forced, as sgemm_strided_batched_variant. */
+int sgemm_batched_variant(int transA, int transB, int M, int N, int K,
+                          float alpha, const float *const *A_array, int lda,
+                                       const float *const *B_array, int ldb,
+                          float beta,        float *const *C_array, int ldc,
+                          int batch, int variant, sgemm_stream_t stream);
+
+/*
+ * Column-major (BLAS convention) forms of sgemm and sgemm_strided_batched:
+ * the same C = alpha * op(A) @ op(B) + beta * C, with
+ *   op(A)[i,k] = transA ? A[i*lda + k] : A[k*lda + i]   (A stored M x K or K x M, by columns)
+ *   op(B)[k,j] = transB ? B[k*ldb + j] : B[j*ldb + k]
+ *   C[i,j]     = C[j*ldc + i]
+ * and lda >= max(1, transA ? K : M), ldb >= max(1, transB ? N : K),
+ * ldc >= max(1, M), each below 2^21. Read by rows, a column-major matrix is
+ * its transpose, so the call runs the row-major kernels on
+ * C^T = op(B)^T @ op(A)^T with the operands swapped: no data moves and the
+ * results are those of the row-major call on the transposed problem.
+ * Status codes, special cases, ownership and accuracy are those of the
+ * row-major forms, positions counted in this argument list.
+ */
+int sgemm_colmajor(int transA, int transB, int M, int N, int K,
+                   float alpha, const float *A, int lda,
+                                const float *B, int ldb,
+                   float beta,        float *C, int ldc,
+                   sgemm_stream_t stream);
+
+int sgemm_colmajor_strided_batched(int transA, int transB, int M, int N, int K,
+                                   float alpha, const float *A, int lda,
+                                                const float *B, int ldb,
+                                   float beta,        float *C, int ldc,
+                                   int batch, long long strideA, long long strideB,
+                                   long long strideC,
+                                   sgemm_stream_t stream);
 
 #ifdef __cplusplus
 }

@@ -16,6 +16,8 @@ import os
 
 __all__ = [
     "SgemmError", "sgemm", "sgemm_strided_batched", "sgemm_strided_batched_variant",
+    "sgemm_batched", "sgemm_batched_variant", "sgemm_colmajor",
+    "sgemm_colmajor_strided_batched", "pointer_array",
     "sgemm_status_string", "sgemm_select_variant", "matmul", "library_path",
     "VARIANT_AUTO", "VARIANT_L256x128", "VARIANT_M128x128", "VARIANT_S64x64",
     "VARIANT_S64x64_V1", "VARIANT_T64x64", "VARIANT_L256x256", "VARIANT_NAMES",
@@ -69,6 +71,15 @@ def _load():
     lib.sgemm_status_string.argtypes = [i]
     lib.sgemm_select_variant.restype = i
     lib.sgemm_select_variant.argtypes = [i, i, i, i, i, i, i, i]
+    lib.sgemm_batched.restype = i
+    lib.sgemm_batched.argtypes = [i, i, i, i, i, f, p, i, p, i, f, p, i, i, p]
+    lib.sgemm_batched_variant.restype = i
+    lib.sgemm_batched_variant.argtypes = [i, i, i, i, i, f, p, i, p, i, f, p, i, i, i, p]
+    lib.sgemm_colmajor.restype = i
+    lib.sgemm_colmajor.argtypes = [i, i, i, i, i, f, p, i, p, i, f, p, i, p]
+    lib.sgemm_colmajor_strided_batched.restype = i
+    lib.sgemm_colmajor_strided_batched.argtypes = [i, i, i, i, i, f, p, i, p, i, f, p, i, i,
+                                                   ll, ll, ll, p]
     _lib = lib
     return lib
 
@@ -85,6 +96,30 @@ def _ptr(x):
             raise TypeError(f"sgemm operands must be float32, got {x.dtype}")
         return x.data_ptr()
     raise TypeError(f"cannot take a device pointer of {type(x).__name__}")
+
+
+def _ptr_array(x):
+    """Device address of a pointer array: an int64 GPU tensor of device
+    addresses (see pointer_array), or an int / None passed through."""
+    if x is None or isinstance(x, int):
+        return x
+    if hasattr(x, "data_ptr"):
+        import torch
+        if not x.is_cuda or x.dtype != torch.int64 or not x.is_contiguous():
+            raise TypeError("a pointer array must be a contiguous int64 GPU tensor")
+        return x.data_ptr()
+    raise TypeError(f"cannot take a device pointer of {type(x).__name__}")
+
+
+def pointer_array(tensors, device=None):
+    """An int64 GPU tensor holding the device addresses of `tensors` (float32
+    GPU tensors, or ints taken as addresses), for the pointer-array form. The
+    caller keeps the tensors alive while the work runs."""
+    import torch
+    addrs = [t if isinstance(t, int) else _ptr(t) for t in tensors]
+    if device is None:
+        device = next((t.device for t in tensors if hasattr(t, "device")), "cuda")
+    return torch.tensor(addrs, dtype=torch.int64).to(device)
 
 
 def _stream(stream, *tensors):
@@ -133,6 +168,47 @@ def sgemm_strided_batched_variant(transA, transB, M, N, K, alpha, A, lda, B, ldb
         int(transA), int(transB), M, N, K, float(alpha), _ptr(A), lda, _ptr(B), ldb,
         float(beta), _ptr(C), ldc, batch, strideA, strideB, strideC, int(variant),
         _stream(stream, A, B, C))
+    return _check(st, check)
+
+
+def sgemm_batched(transA, transB, M, N, K, alpha, A_array, lda, B_array, ldb, beta, C_array,
+                  ldc, batch, stream=None, check=True) -> int:
+    """C ABI ``sgemm_batched``; the arrays are int64 GPU tensors of device
+    addresses (see pointer_array) or raw device pointers."""
+    st = _load().sgemm_batched(int(transA), int(transB), M, N, K, float(alpha),
+                               _ptr_array(A_array), lda, _ptr_array(B_array), ldb, float(beta),
+                               _ptr_array(C_array), ldc, batch,
+                               _stream(stream, A_array, B_array, C_array))
+    return _check(st, check)
+
+
+def sgemm_batched_variant(transA, transB, M, N, K, alpha, A_array, lda, B_array, ldb, beta,
+                          C_array, ldc, batch, variant, stream=None, check=True) -> int:
+    """C ABI ``sgemm_batched_variant`` (kernel variant forced)."""
+    st = _load().sgemm_batched_variant(int(transA), int(transB), M, N, K, float(alpha),
+                                       _ptr_array(A_array), lda, _ptr_array(B_array), ldb,
+                                       float(beta), _ptr_array(C_array), ldc, batch,
+                                       int(variant), _stream(stream, A_array, B_array, C_array))
+    return _check(st, check)
+
+
+def sgemm_colmajor(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream=None,
+                   check=True) -> int:
+    """C ABI ``sgemm_colmajor`` (BLAS column-major storage)."""
+    st = _load().sgemm_colmajor(int(transA), int(transB), M, N, K, float(alpha), _ptr(A), lda,
+                                _ptr(B), ldb, float(beta), _ptr(C), ldc,
+                                _stream(stream, A, B, C))
+    return _check(st, check)
+
+
+def sgemm_colmajor_strided_batched(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
+                                   batch, strideA, strideB, strideC, stream=None,
+                                   check=True) -> int:
+    """C ABI ``sgemm_colmajor_strided_batched``."""
+    st = _load().sgemm_colmajor_strided_batched(int(transA), int(transB), M, N, K, float(alpha),
+                                                _ptr(A), lda, _ptr(B), ldb, float(beta),
+                                                _ptr(C), ldc, batch, strideA, strideB, strideC,
+                                                _stream(stream, A, B, C))
     return _check(st, check)
 
 

@@ -61,18 +61,57 @@ constexpr int kRsrcWord3 = 0x00020000;     // gfx9 raw buffer, 32-bit data forma
 constexpr int kNumXcd = 8;                 // MI355X: 8 XCDs x 32 CUs
 constexpr int kMaxLd = (1 << 21) - 1;      // keeps (255*ld + 256)*4 < 2^31
 
+// Batch item b's operands are A + b*sA, B + b*sB, C + b*sC, or, where the
+// pointer-array form supplies them, Aarr[b], Barr[b], Carr[b].
 struct Params {
     const float *A;
     const float *B;
     float *C;
+    const float *const *Aarr;
+    const float *const *Barr;
+    float *const *Carr;
     int M, N, K;
     int lda, ldb, ldc;
     long long sA, sB, sC;
     float alpha, beta;
-    int batch;       // batch items covered by this launch
     int tiles_m, tiles_n;
     int group_m;
 };
+
+__device__ __forceinline__ const float *item_a(const Params &p, int b)
+{
+    return p.Aarr ? p.Aarr[b] : p.A + b * p.sA;
+}
+__device__ __forceinline__ const float *item_b(const Params &p, int b)
+{
+    return p.Barr ? p.Barr[b] : p.B + b * p.sB;
+}
+__device__ __forceinline__ float *item_c(const Params &p, int b)
+{
+    return p.Carr ? p.Carr[b] : p.C + b * p.sC;
+}
+
+// One output tile the plain way, for a batch item whose A or B pointer does
+// not allow the 16-byte loads its kernel was built for (only reachable in the
+// pointer-array form, where the host cannot see the item pointers): every
+// thread walks whole dot products over k with 4-byte loads.
+template <int BM, int BN, int NT, bool A_KC, bool B_KC>
+__device__ void plain_tile(const Params &p, const float *Ab, const float *Bb, float *Cb, int m0,
+                           int n0)
+{
+    for (int e = threadIdx.x; e < BM * BN; e += NT) {
+        const int i = m0 + e / BN, j = n0 + e % BN;
+        if (i >= p.M || j >= p.N)
+            continue;
+        const long long sa_i = A_KC ? (long long)i * p.lda : i, sa_k = A_KC ? 1 : p.lda;
+        const long long sb_j = B_KC ? (long long)j * p.ldb : j, sb_k = B_KC ? 1 : p.ldb;
+        float acc = 0.0f;
+        for (int k = 0; k < p.K; ++k)
+            acc = __builtin_fmaf(Ab[sa_i + k * sa_k], Bb[sb_j + k * sb_k], acc);
+        float *c = Cb + (long long)i * p.ldc + j;
+        *c = p.beta == 0.0f ? p.alpha * acc : p.alpha * acc + p.beta * *c;
+    }
+}
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const float *base, long long elems)
 {
@@ -282,8 +321,15 @@ sgemm_mfma_kernel(Params p)
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm0 = (wave % WAVES_M) * WM, wn0 = (wave / WAVES_M) * WN;
 
+    const float *Ab = item_a(p, b), *Bb = item_b(p, b);
+    float *Cb = item_c(p, b);
+    if (VEC == 4 && (((uintptr_t)Ab | (uintptr_t)Bb) & 15u)) {
+        plain_tile<BM, BN, NT, A_KC, B_KC>(p, Ab, Bb, Cb, m0, n0);
+        return;
+    }
+
     OpA opa;
-    opa.X = p.A + b * p.sA;
+    opa.X = Ab;
     opa.ld = p.lda;
     opa.total = A_KC ? (long long)(p.M - 1) * p.lda + p.K : (long long)(p.K - 1) * p.lda + p.M;
     opa.O = p.M;
@@ -291,7 +337,7 @@ sgemm_mfma_kernel(Params p)
     opa.o0 = m0;
     opa.init(tid);
     OpB opb;
-    opb.X = p.B + b * p.sB;
+    opb.X = Bb;
     opb.ld = p.ldb;
     opb.total = B_KC ? (long long)(p.N - 1) * p.ldb + p.K : (long long)(p.K - 1) * p.ldb + p.N;
     opb.O = p.N;
@@ -420,7 +466,6 @@ sgemm_mfma_kernel(Params p)
     // Epilogue: C = alpha * acc + beta * C, lanes outside M x N dropped.
     // Accumulator register v of lane l holds row 8*(v/4) + 4*(l/32) + v%4,
     // column l%32 of its 32 x 32 product.
-    float *Cb = p.C + b * p.sC;
     const long long cbase = (long long)m0 * p.ldc + n0;
     const __amdgpu_buffer_rsrc_t rc =
         make_rsrc(Cb + cbase, (long long)(p.M - 1) * p.ldc + p.N - cbase);
@@ -607,8 +652,15 @@ sgemm_stream_kernel(Params p)
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
+    const float *Ab = item_a(p, b), *Bb = item_b(p, b);
+    float *Cb = item_c(p, b);
+    if (((uintptr_t)Ab | (uintptr_t)Bb) & 15u) {
+        plain_tile<BM, BN, 64 * WAVES, A_KC, B_KC>(p, Ab, Bb, Cb, m0, n0);
+        return;
+    }
+
     OpA opa;
-    opa.X = p.A + b * p.sA;
+    opa.X = Ab;
     opa.ld = p.lda;
     opa.total = A_KC ? (long long)(p.M - 1) * p.lda + p.K : (long long)(p.K - 1) * p.lda + p.M;
     opa.O = p.M;
@@ -616,7 +668,7 @@ sgemm_stream_kernel(Params p)
     opa.o0 = m0;
     opa.init(lane, wave * BK, WAVES * BK);
     OpB opb;
-    opb.X = p.B + b * p.sB;
+    opb.X = Bb;
     opb.ld = p.ldb;
     opb.total = B_KC ? (long long)(p.N - 1) * p.ldb + p.K : (long long)(p.K - 1) * p.ldb + p.N;
     opb.O = p.N;
@@ -712,7 +764,6 @@ sgemm_stream_kernel(Params p)
         for (int e = 0; e < 4; ++e)
             sum[c + e] = x[e];
     }
-    float *Cb = p.C + b * p.sC;
     const long long cbase = (long long)m0 * p.ldc + n0;
     const __amdgpu_buffer_rsrc_t rc =
         make_rsrc(Cb + cbase, (long long)(p.M - 1) * p.ldc + p.N - cbase);
@@ -739,15 +790,16 @@ sgemm_stream_kernel(Params p)
 }
 
 // C = beta * C over the M x N window of every batch item (alpha == 0 or K == 0).
-__global__ void __launch_bounds__(256) sgemm_scale_kernel(float *C, int M, int N, int ldc,
-                                                          long long sC, int batch, float beta)
+__global__ void __launch_bounds__(256) sgemm_scale_kernel(float *C, float *const *Carr, int M,
+                                                          int N, int ldc, long long sC,
+                                                          int batch, float beta)
 {
     const long long per = (long long)M * N;
     const long long total = per * batch;
     for (long long e = blockIdx.x * 256LL + threadIdx.x; e < total;
          e += (long long)gridDim.x * 256) {
         const long long b = e / per, r = (e % per) / N, c = e % N;
-        float *x = C + b * sC + r * ldc + c;
+        float *x = (Carr ? Carr[b] : C + b * sC) + r * ldc + c;
         *x = beta == 0.0f ? 0.0f : beta * *x;
     }
 }
@@ -903,45 +955,57 @@ extern "C" int sgemm_select_variant(int transA, int transB, int M, int N, int K,
     return best;
 }
 
-extern "C" int sgemm_strided_batched_variant(int transA, int transB, int M, int N, int K,
-                                             float alpha, const float *A, int lda,
-                                             const float *B, int ldb, float beta, float *C,
-                                             int ldc, int batch, long long strideA,
-                                             long long strideB, long long strideC, int variant,
-                                             sgemm_stream_t stream)
-{
-    int st = validate(transA, transB, M, N, K, A, lda, B, ldb, C, ldc, batch, strideA, strideB,
-                      strideC, alpha, beta);
-    if (st != 0)
-        return st;
-    if (variant < SGEMM_VARIANT_AUTO || variant >= SGEMM_VARIANT_COUNT)
-        return -18;
-    if (M == 0 || N == 0 || batch == 0)
-        return 0;
-    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+namespace {
 
-    if (K == 0 || alpha == 0.0f) {
-        if (beta == 1.0f)
+// One validated call in row-major terms. Either the strided bases (A, B, C
+// with sA, sB, sC) or the pointer arrays (Aarr, Barr, Carr) describe the
+// batch items.
+struct Call {
+    int tA, tB, M, N, K;
+    float alpha, beta;
+    const float *A, *B;
+    float *C;
+    int lda, ldb, ldc, batch;
+    long long sA, sB, sC;
+    const float *const *Aarr;
+    const float *const *Barr;
+    float *const *Carr;
+};
+
+int launch(const Call &c, int variant, hipStream_t s)
+{
+    if (c.M == 0 || c.N == 0 || c.batch == 0)
+        return 0;
+    if (c.K == 0 || c.alpha == 0.0f) {
+        if (c.beta == 1.0f)
             return 0;
-        const long long total = (long long)M * N * batch;
+        const long long total = (long long)c.M * c.N * c.batch;
         const long long blocks = ceil_div(total, 256) < 8192 ? ceil_div(total, 256) : 8192;
-        void *args[] = {&C, &M, &N, &ldc, &strideC, &batch, &beta};
+        float *C = c.C;
+        float *const *Carr = c.Carr;
+        int M = c.M, N = c.N, ldc = c.ldc, batch = c.batch;
+        long long sC = c.sC;
+        float beta = c.beta;
+        void *args[] = {&C, &Carr, &M, &N, &ldc, &sC, &batch, &beta};
         return (int)hipLaunchKernel((const void *)sgemm_scale_kernel, dim3((unsigned)blocks),
                                     dim3(256), args, 0, s);
     }
 
     // 16-byte loads need aligned bases, ld and batch strides, and whole
-    // 4-float chunks along each operand's contiguous dimension.
-    const bool a_kc = transA == 0, b_kc = transB == 1;
-    const bool vec4_ok = aligned16(A) && aligned16(B) && lda % 4 == 0 && ldb % 4 == 0 &&
-                         strideA % 4 == 0 && strideB % 4 == 0 &&
-                         (a_kc ? K % 4 == 0 : M % 4 == 0) && (b_kc ? K % 4 == 0 : N % 4 == 0);
+    // 4-float chunks along each operand's contiguous dimension. Item pointers
+    // of the pointer-array form are not visible here; the kernels check them.
+    const bool arrays = c.Aarr != nullptr;
+    const bool a_kc = c.tA == 0, b_kc = c.tB == 1;
+    const bool vec4_ok =
+        (arrays || (aligned16(c.A) && aligned16(c.B) && c.sA % 4 == 0 && c.sB % 4 == 0)) &&
+        c.lda % 4 == 0 && c.ldb % 4 == 0 && (a_kc ? c.K % 4 == 0 : c.M % 4 == 0) &&
+        (b_kc ? c.K % 4 == 0 : c.N % 4 == 0);
     if (variant == SGEMM_VARIANT_AUTO) {
         int cus = 0;
-        st = num_cus_of_current_device(&cus);
+        const int st = num_cus_of_current_device(&cus);
         if (st != 0)
             return st;
-        variant = sgemm_select_variant(transA, transB, M, N, K, batch, vec4_ok ? 1 : 0, cus);
+        variant = sgemm_select_variant(c.tA, c.tB, c.M, c.N, c.K, c.batch, vec4_ok ? 1 : 0, cus);
         if (variant < 0)
             return variant;
     } else if (kVariants[variant].vec == 4 && !vec4_ok) {
@@ -949,24 +1013,27 @@ extern "C" int sgemm_strided_batched_variant(int transA, int transB, int M, int 
     }
 
     const VariantInfo &vi = kVariants[variant];
-    const int even_k = K % kBK == 0 ? 1 : 0;
+    const int even_k = c.K % kBK == 0 ? 1 : 0;
     Params p;
-    p.A = A;
-    p.B = B;
-    p.C = C;
-    p.M = M;
-    p.N = N;
-    p.K = K;
-    p.lda = lda;
-    p.ldb = ldb;
-    p.ldc = ldc;
-    p.sA = strideA;
-    p.sB = strideB;
-    p.sC = strideC;
-    p.alpha = alpha;
-    p.beta = beta;
-    p.tiles_m = (int)ceil_div(M, vi.bm);
-    p.tiles_n = (int)ceil_div(N, vi.bn);
+    p.A = c.A;
+    p.B = c.B;
+    p.C = c.C;
+    p.Aarr = c.Aarr;
+    p.Barr = c.Barr;
+    p.Carr = c.Carr;
+    p.M = c.M;
+    p.N = c.N;
+    p.K = c.K;
+    p.lda = c.lda;
+    p.ldb = c.ldb;
+    p.ldc = c.ldc;
+    p.sA = c.sA;
+    p.sB = c.sB;
+    p.sC = c.sC;
+    p.alpha = c.alpha;
+    p.beta = c.beta;
+    p.tiles_m = (int)ceil_div(c.M, vi.bm);
+    p.tiles_n = (int)ceil_div(c.N, vi.bn);
     p.group_m = 8;
     const long long per_batch = (long long)p.tiles_m * p.tiles_n;
     // Keep one launch's workgroup count within 2^31 and its batch axis within 65535.
@@ -975,14 +1042,19 @@ extern "C" int sgemm_strided_batched_variant(int transA, int transB, int M, int 
         max_items = 65535;
     if (max_items < 1)
         return -3;
-    KernelFn fn = vi.fn[transA][transB][even_k];
-    for (long long b0 = 0; b0 < batch; b0 += max_items) {
-        const long long nb = batch - b0 < max_items ? batch - b0 : max_items;
+    KernelFn fn = vi.fn[c.tA][c.tB][even_k];
+    for (long long b0 = 0; b0 < c.batch; b0 += max_items) {
+        const long long nb = c.batch - b0 < max_items ? c.batch - b0 : max_items;
         Params q = p;
-        q.A = A + b0 * strideA;
-        q.B = B + b0 * strideB;
-        q.C = C + b0 * strideC;
-        q.batch = (int)nb;
+        if (arrays) {
+            q.Aarr = c.Aarr + b0;
+            q.Barr = c.Barr + b0;
+            q.Carr = c.Carr + b0;
+        } else {
+            q.A = c.A + b0 * c.sA;
+            q.B = c.B + b0 * c.sB;
+            q.C = c.C + b0 * c.sC;
+        }
         void *args[] = {&q};
         hipError_t e = hipLaunchKernel((const void *)fn, dim3((unsigned)per_batch, (unsigned)nb),
                                        dim3(vi.threads), args, 0, s);
@@ -990,6 +1062,55 @@ extern "C" int sgemm_strided_batched_variant(int transA, int transB, int M, int 
             return (int)e;
     }
     return 0;
+}
+
+// Column-major arguments checked in their own positions (the same positions
+// as the row-major entry points): stored row lengths follow the BLAS
+// convention, op(A) M x K with A stored M x K (transA = 0) or K x M, and so on.
+int validate_colmajor(int tA, int tB, int M, int N, int K, const float *A, int lda,
+                      const float *B, int ldb, const float *C, int ldc, int batch, long long sA,
+                      long long sB, long long sC, float alpha, float beta)
+{
+    if (tA != 0 && tA != 1) return -1;
+    if (tB != 0 && tB != 1) return -2;
+    if (M < 0) return -3;
+    if (N < 0) return -4;
+    if (K < 0) return -5;
+    const int colA = tA ? K : M, colB = tB ? N : K;
+    if (lda < (colA > 1 ? colA : 1) || lda > kMaxLd) return -8;
+    if (ldb < (colB > 1 ? colB : 1) || ldb > kMaxLd) return -10;
+    if (ldc < (M > 1 ? M : 1) || ldc > kMaxLd) return -13;
+    if (batch < 0) return -14;
+    if (sA < 0) return -15;
+    if (sB < 0) return -16;
+    if (sC < 0) return -17;
+    const bool work = M > 0 && N > 0 && batch > 0;
+    const bool product = work && K > 0 && alpha != 0.0f;
+    const bool touch_c = work && (product || beta != 1.0f);
+    if (product && A == nullptr) return -7;
+    if (product && B == nullptr) return -9;
+    if (touch_c && C == nullptr) return -12;
+    return 0;
+}
+
+} // namespace
+
+extern "C" int sgemm_strided_batched_variant(int transA, int transB, int M, int N, int K,
+                                             float alpha, const float *A, int lda,
+                                             const float *B, int ldb, float beta, float *C,
+                                             int ldc, int batch, long long strideA,
+                                             long long strideB, long long strideC, int variant,
+                                             sgemm_stream_t stream)
+{
+    const int st = validate(transA, transB, M, N, K, A, lda, B, ldb, C, ldc, batch, strideA,
+                            strideB, strideC, alpha, beta);
+    if (st != 0)
+        return st;
+    if (variant < SGEMM_VARIANT_AUTO || variant >= SGEMM_VARIANT_COUNT)
+        return -18;
+    const Call c{transA, transB, M, N, K, alpha, beta, A, B, C, lda, ldb, ldc, batch,
+                 strideA, strideB, strideC, nullptr, nullptr, nullptr};
+    return launch(c, variant, reinterpret_cast<hipStream_t>(stream));
 }
 
 extern "C" int sgemm_strided_batched(int transA, int transB, int M, int N, int K, float alpha,
@@ -1010,6 +1131,68 @@ extern "C" int sgemm(int transA, int transB, int M, int N, int K, float alpha, c
                                  0, 0, 0, stream);
 }
 
+extern "C" int sgemm_batched_variant(int transA, int transB, int M, int N, int K, float alpha,
+                                     const float *const *A_array, int lda,
+                                     const float *const *B_array, int ldb, float beta,
+                                     float *const *C_array, int ldc, int batch, int variant,
+                                     sgemm_stream_t stream)
+{
+    // The arrays stand in for the operands in the NULL checks; the item
+    // pointers they hold live in device memory and are not inspected here.
+    const int st = validate(transA, transB, M, N, K, reinterpret_cast<const float *>(A_array),
+                            lda, reinterpret_cast<const float *>(B_array), ldb,
+                            reinterpret_cast<const float *>(C_array), ldc, batch, 0, 0, 0, alpha,
+                            beta);
+    if (st != 0)
+        return st;
+    if (variant < SGEMM_VARIANT_AUTO || variant >= SGEMM_VARIANT_COUNT)
+        return -18;
+    // alpha == 0 or K == 0 reads neither A_array nor B_array, which may then be NULL.
+    const bool product = K > 0 && alpha != 0.0f;
+    const Call c{transA, transB, M, N, K, alpha, beta, nullptr, nullptr, nullptr, lda, ldb, ldc,
+                 batch, 0, 0, 0, product ? A_array : nullptr, product ? B_array : nullptr,
+                 C_array};
+    return launch(c, variant, reinterpret_cast<hipStream_t>(stream));
+}
+
+extern "C" int sgemm_batched(int transA, int transB, int M, int N, int K, float alpha,
+                             const float *const *A_array, int lda, const float *const *B_array,
+                             int ldb, float beta, float *const *C_array, int ldc, int batch,
+                             sgemm_stream_t stream)
+{
+    return sgemm_batched_variant(transA, transB, M, N, K, alpha, A_array, lda, B_array, ldb, beta,
+                                 C_array, ldc, batch, SGEMM_VARIANT_AUTO, stream);
+}
+
+extern "C" int sgemm_colmajor_strided_batched(int transA, int transB, int M, int N, int K,
+                                              float alpha, const float *A, int lda,
+                                              const float *B, int ldb, float beta, float *C,
+                                              int ldc, int batch, long long strideA,
+                                              long long strideB, long long strideC,
+                                              sgemm_stream_t stream)
+{
+    const int st = validate_colmajor(transA, transB, M, N, K, A, lda, B, ldb, C, ldc, batch,
+                                     strideA, strideB, strideC, alpha, beta);
+    if (st != 0)
+        return st;
+    // A column-major C (M x N, ld ldc) is, read row-major, C^T (N x M) with the
+    // same ld, and C^T = op(B)^T op(A)^T: the row-major product with the
+    // operands swapped. A column-major B read row-major is B^T, so op(B)^T is
+    // stored exactly as a row-major operand with the same transpose flag, and
+    // likewise for A.
+    const Call c{transB, transA, N, M, K, alpha, beta, B, A, C, ldb, lda, ldc, batch,
+                 strideB, strideA, strideC, nullptr, nullptr, nullptr};
+    return launch(c, SGEMM_VARIANT_AUTO, reinterpret_cast<hipStream_t>(stream));
+}
+
+extern "C" int sgemm_colmajor(int transA, int transB, int M, int N, int K, float alpha,
+                              const float *A, int lda, const float *B, int ldb, float beta,
+                              float *C, int ldc, sgemm_stream_t stream)
+{
+    return sgemm_colmajor_strided_batched(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C,
+                                          ldc, 1, 0, 0, 0, stream);
+}
+
 extern "C" const char *sgemm_status_string(int status)
 {
     switch (status) {
@@ -1019,17 +1202,17 @@ extern "C" const char *sgemm_status_string(int status)
     case -3: return "invalid argument 3 (M < 0)";
     case -4: return "invalid argument 4 (N < 0)";
     case -5: return "invalid argument 5 (K < 0)";
-    case -7: return "invalid argument 7 (A is NULL)";
+    case -7: return "invalid argument 7 (A or A_array is NULL)";
     case -8: return "invalid argument 8 (lda below the stored row length or >= 2^21)";
-    case -9: return "invalid argument 9 (B is NULL)";
+    case -9: return "invalid argument 9 (B or B_array is NULL)";
     case -10: return "invalid argument 10 (ldb below the stored row length or >= 2^21)";
-    case -12: return "invalid argument 12 (C is NULL)";
-    case -13: return "invalid argument 13 (ldc < max(1, N) or >= 2^21)";
+    case -12: return "invalid argument 12 (C or C_array is NULL)";
+    case -13: return "invalid argument 13 (ldc below the stored row length or >= 2^21)";
     case -14: return "invalid argument 14 (batch < 0)";
     case -15: return "invalid argument 15 (strideA < 0)";
     case -16: return "invalid argument 16 (strideB < 0)";
     case -17: return "invalid argument 17 (strideC < 0)";
-    case -18: return "invalid argument 18 (unknown variant, or a 4-float variant for unaligned operands)";
+    case -18: return "invalid variant argument (unknown variant, or a 4-float variant for unaligned operands)";
     default: break;
     }
     if (status < 0)

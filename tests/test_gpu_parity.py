@@ -388,3 +388,206 @@ def test_degenerate_shapes(env, shape):
         st, got = run_gpu(env, w, A, B, C)
         assert st == 0
         check_against_oracle(w, A, B, C, got, exact=True)
+
+
+# ------------------------------------------------------------------ pointer-array batched
+
+def run_pointer_array(env, tA, tB, M, N, K, alpha, beta, lda, ldb, ldc, batch, seed, dist,
+                      misalign=(), shared_a=(), variant=-1):
+    """Items scattered through three device pools at irregular (16-byte
+    aligned) offsets; items listed in `misalign` are shifted one float off
+    16-byte alignment; items listed in `shared_a` reuse item 0's A. Returns
+    the status and a list of (A, B, C_in, C_out) per item."""
+    torch, pg = env
+    dev = torch.device("cuda:0")
+    rng = np.random.default_rng(seed)
+    items = []
+    for b in range(batch):
+        w = Workload("item", tA, tB, M, N, K, alpha, beta, seed=seed * 1000 + b, dist=dist,
+                     lda=lda, ldb=ldb, ldc=ldc)
+        items.append(workloads.make_inputs(w))
+    shared = set(shared_a)
+
+    def layout(sizes, skip=()):
+        offs, pos = [], GUARD
+        for b, n in enumerate(sizes):
+            if b in skip:
+                offs.append(offs[0])
+                continue
+            pos += 4 * int(rng.integers(0, 9))          # irregular gaps, 16-byte aligned
+            offs.append(pos + (1 if b in misalign else 0))
+            pos = offs[-1] + n
+            pos = (pos + 3) // 4 * 4
+        return offs, pos + GUARD
+
+    offA, nA = layout([it[0].size for it in items], skip=shared)
+    offB, nB = layout([it[1].size for it in items])
+    offC, nC = layout([it[2].size for it in items])
+    pools = []
+    for offs, n, k in ((offA, nA, 0), (offB, nB, 1), (offC, nC, 2)):
+        host = np.full(n, -7.25, np.float32)
+        for b, o in enumerate(offs):
+            if k == 0 and b in shared:
+                continue
+            host[o:o + items[b][k].size] = items[b][k]
+        pools.append((host, torch.from_numpy(host).to(dev)))
+    ptrs = [pg.pointer_array([p[1].data_ptr() + 4 * o for o in offs], dev)
+            for p, offs in zip(pools, (offA, offB, offC))]
+    st = pg.sgemm_batched_variant(tA, tB, M, N, K, alpha, ptrs[0], lda, ptrs[1], ldb, beta,
+                                  ptrs[2], ldc, batch, variant, check=False)
+    torch.cuda.synchronize(dev)
+    outC = pools[2][1].cpu().numpy()
+    # every float of the C pool outside the items' M x N windows keeps its bits
+    mask = np.zeros(nC, bool)
+    for o in offC:
+        if M and N:
+            mask[(o + np.arange(M)[:, None] * ldc + np.arange(N)[None, :]).reshape(-1)] = True
+    assert np.array_equal(outC[~mask].view(np.uint32), pools[2][0][~mask].view(np.uint32)), \
+        "the C pool changed outside the items' windows"
+    res = []
+    for b in range(batch):
+        A = items[0][0] if b in shared else items[b][0]
+        res.append((A, items[b][1], items[b][2], outC[offC[b]:offC[b] + items[b][2].size]))
+    return st, res
+
+
+def check_items(tA, tB, M, N, K, alpha, beta, lda, ldb, ldc, res, exact):
+    w = Workload("item", tA, tB, M, N, K, alpha, beta, seed=0, lda=lda, ldb=ldb, ldc=ldc)
+    for A, B, C, got in res:
+        check_against_oracle(w, A, B, C, got, exact=exact)
+
+
+@pytest.mark.parametrize("variant", [-1, 0, 1, 2, 3, 4, 5])
+def test_pointer_array_bitwise(env, variant):
+    """Pointer-array batches on every variant and transpose pair, integer
+    inputs: bitwise equal to the oracle run item by item, with a shared A
+    item and padded leading dimensions."""
+    for (M, N, K), (tA, tB) in itertools.product([(68, 132, 40), (260, 36, 20), (12, 8, 100)],
+                                                 itertools.product([0, 1], repeat=2)):
+        lda, ldb, ldc = (M if tA else K) + 4, (K if tB else N) + 8, N + 4
+        log(f"[ptr-array] variant {variant} {M}x{N}x{K} tA={tA} tB={tB}")
+        st, res = run_pointer_array(env, tA, tB, M, N, K, 2.0, -1.0, lda, ldb, ldc, batch=5,
+                                    seed=M + N + K + 2 * tA + tB, dist="int3", shared_a=(3,),
+                                    variant=variant)
+        assert st == 0, st
+        check_items(tA, tB, M, N, K, 2.0, -1.0, lda, ldb, ldc, res, exact=True)
+
+
+@pytest.mark.parametrize("variant", [-1, 0, 2, 4, 5])
+def test_pointer_array_misaligned_items(env, variant):
+    """Items whose A or B is not 16-byte aligned, in a launch of a 4-float
+    kernel: those items take the kernel's plain per-element path and must
+    still be exact; their aligned neighbours take the MFMA path."""
+    M, N, K = 72, 100, 48
+    st, res = run_pointer_array(env, 0, 0, M, N, K, 1.0, 0.5, K, N, N, batch=6, seed=31,
+                                dist="int3", misalign=(1, 4), variant=variant)
+    assert st == 0
+    check_items(0, 0, M, N, K, 1.0, 0.5, K, N, N, res, exact=True)
+    st, res = run_pointer_array(env, 1, 1, M, N, K, -0.5, 0.0, M, K, N, batch=4, seed=32,
+                                dist="normal", misalign=(0, 3), variant=variant)
+    assert st == 0
+    check_items(1, 1, M, N, K, -0.5, 0.0, M, K, N, res, exact=False)
+
+
+def test_pointer_array_float_and_special_cases(env):
+    """fp32 inputs within the bound; alpha = 0 and K = 0 scale each C item
+    through the array without reading A or B (NULL arrays allowed)."""
+    torch, pg = env
+    st, res = run_pointer_array(env, 0, 1, 300, 200, 150, 0.75, -1.5, 152, 152, 204, batch=3,
+                                seed=33, dist="normal")
+    assert st == 0
+    check_items(0, 1, 300, 200, 150, 0.75, -1.5, 152, 152, 204, res, exact=False)
+    for alpha, K in ((0.0, 30), (1.0, 0)):
+        dev = torch.device("cuda:0")
+        C = [torch.randn(40, 24, device=dev) for _ in range(3)]
+        before = [c.clone() for c in C]
+        st = pg.sgemm_batched(0, 0, 40, 24, K, alpha, None, max(K, 1), None, 24, -2.0,
+                              pg.pointer_array(C), 24, 3, check=False)
+        torch.cuda.synchronize(dev)
+        assert st == 0
+        for c, c0 in zip(C, before):
+            assert torch.equal(c, c0 * -2.0)
+
+
+# ------------------------------------------------------------------ column-major
+
+def colmajor_store(X, ld, cols):
+    """Column-major storage of the 2-D array X (rows x cols) with leading
+    dimension ld: element (r, c) at r + c*ld. The buffer ends at the last
+    stored element."""
+    rows = X.shape[0]
+    buf = np.full((cols - 1) * ld + rows if rows and cols else 0, -7.25, np.float32)
+    for c in range(cols):
+        buf[c * ld:c * ld + rows] = X[:, c]
+    return buf
+
+
+@pytest.mark.parametrize("tA,tB", list(itertools.product([0, 1], repeat=2)))
+def test_colmajor_against_definition(env, tA, tB):
+    """The column-major entry points: operands stored by columns as the
+    header's index formulas say, results compared with the oracle on the
+    same logical matrices (row-major, untransposed). Integer inputs are
+    bitwise, fp32 inputs within the bound; the strided form checks two
+    items with gaps."""
+    torch, pg = env
+    dev = torch.device("cuda:0")
+    for (M, N, K), dist in (((68, 132, 36), "int3"), ((257, 129, 65), "normal"),
+                            ((4, 300, 8), "int3")):
+        # integer cases keep every ld and stride a multiple of 4 (4-float
+        # kernels); the fp32 case has odd ones (1-float kernels)
+        aligned = dist == "int3"
+        r4 = (lambda n: (n + 3) // 4 * 4 + 4) if aligned else (lambda n: n + 3)
+        rng = np.random.default_rng(M * N + K + tA + 2 * tB)
+        draw = (lambda *s: rng.integers(-3, 4, s).astype(np.float32)) if dist == "int3" else \
+            (lambda *s: rng.standard_normal(s).astype(np.float32))
+        batch = 2
+        Aop = [draw(M, K) for _ in range(batch)]     # op(A) as a logical M x K matrix
+        Bop = [draw(K, N) for _ in range(batch)]     # op(B) as a logical K x N matrix
+        Cm = [draw(M, N) for _ in range(batch)]
+        alpha, beta = (2.0, -1.0) if dist == "int3" else (0.75, 1.5)
+        # stored matrices: transA = 0 keeps op(A) (M x K by columns), 1 stores its
+        # transpose; likewise for B
+        As = [a.T.copy() if tA else a for a in Aop]
+        Bs = [b.T.copy() if tB else b for b in Bop]
+        lda, ldb, ldc = r4(As[0].shape[0]), r4(Bs[0].shape[0]), r4(M)
+        bufA = [colmajor_store(a, lda, a.shape[1]) for a in As]
+        bufB = [colmajor_store(b, ldb, b.shape[1]) for b in Bs]
+        bufC = [colmajor_store(c, ldc, N) for c in Cm]
+        sA, sB, sC = (r4(len(x[0])) for x in (bufA, bufB, bufC))
+
+        def pack(bufs, stride):
+            out = np.full(stride * (batch - 1) + len(bufs[-1]), -7.25, np.float32)
+            for b, x in enumerate(bufs):
+                out[b * stride:b * stride + len(x)] = x
+            return out
+        hA, hB, hC = pack(bufA, sA), pack(bufB, sB), pack(bufC, sC)
+        dA, dB = (torch.from_numpy(x).to(dev) for x in (hA, hB))
+        for form in ("single", "strided"):
+            dC = torch.from_numpy(hC).to(dev)
+            log(f"[colmajor] {form} {M}x{N}x{K} tA={tA} tB={tB} {dist}")
+            if form == "single":
+                st = pg.sgemm_colmajor(tA, tB, M, N, K, alpha, dA, lda, dB, ldb, beta, dC, ldc,
+                                       check=False)
+                items = 1
+            else:
+                st = pg.sgemm_colmajor_strided_batched(tA, tB, M, N, K, alpha, dA, lda, dB,
+                                                       ldb, beta, dC, ldc, batch, sA, sB, sC,
+                                                       check=False)
+                items = batch
+            torch.cuda.synchronize(dev)
+            assert st == 0
+            out = dC.cpu().numpy()
+            written = np.zeros(out.size, bool)
+            for b in range(items):
+                idx = b * sC + np.arange(M)[:, None] + np.arange(N)[None, :] * ldc
+                written[idx.reshape(-1)] = True
+                got = out[idx]
+                ref, S = oracle.sgemm_rows(0, 0, M, N, K, alpha, Aop[b].reshape(-1), K,
+                                           Bop[b].reshape(-1), N, beta, Cm[b].reshape(-1), N)
+                ref, S = ref.reshape(M, N), S.reshape(M, N)
+                if dist == "int3":
+                    assert np.array_equal(got, ref.astype(np.float32)), (form, b)
+                else:
+                    rep = oracle.bound_check(got, ref, S, Cm[b], alpha, beta, K)
+                    assert rep.ok, (form, b, rep)
+            assert np.array_equal(out[~written].view(np.uint32), hC[~written].view(np.uint32))
