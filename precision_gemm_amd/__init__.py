@@ -20,7 +20,8 @@ __all__ = [
     "sgemm_colmajor_strided_batched", "pointer_array",
     "sgemm_status_string", "sgemm_select_variant", "matmul", "library_path",
     "VARIANT_AUTO", "VARIANT_L256x128", "VARIANT_M128x128", "VARIANT_S64x64",
-    "VARIANT_S64x64_V1", "VARIANT_T64x64", "VARIANT_L256x256", "VARIANT_NAMES",
+    "VARIANT_S64x64_V1", "VARIANT_T64x64", "VARIANT_L256x256", "VARIANT_S64x64_K2",
+    "VARIANT_COUNT", "VARIANT_NAMES",
 ]
 
 VARIANT_AUTO = -1
@@ -30,8 +31,10 @@ VARIANT_S64x64 = 2
 VARIANT_S64x64_V1 = 3
 VARIANT_T64x64 = 4
 VARIANT_L256x256 = 5
+VARIANT_S64x64_K2 = 6
+VARIANT_COUNT = 7
 VARIANT_NAMES = {0: "L256x128", 1: "M128x128", 2: "S64x64", 3: "S64x64_V1", 4: "T64x64",
-                 5: "L256x256"}
+                 5: "L256x256", 6: "S64x64_K2"}
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _lib = None

@@ -297,17 +297,26 @@ __device__ __forceinline__ void tile_of(const Params &p, int &b, int &tm, int &t
     tn = (t % in_group) / gsize;
 }
 
-template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int MIN_WAVES_PER_EU,
+// WAVES_K = 2 splits every K-step between two groups of WAVES_M x WAVES_N
+// waves: group g multiplies the k-groups [g*NQ/2, (g+1)*NQ/2) of each stage
+// into its own accumulators, which gives every SIMD two waves on a tile that
+// would otherwise leave one. The two partial tiles are added through LDS at
+// the end in a fixed order (group 0's plus group 1's), so results do not
+// depend on timing.
+template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int WAVES_K, int MIN_WAVES_PER_EU,
           bool A_KC, bool B_KC, bool EVEN_K, int VEC>
 __global__ void
-__attribute__((amdgpu_flat_work_group_size(64 * WAVES_M * WAVES_N, 64 * WAVES_M * WAVES_N),
+__attribute__((amdgpu_flat_work_group_size(64 * WAVES_M * WAVES_N * WAVES_K,
+                                           64 * WAVES_M * WAVES_N * WAVES_K),
                amdgpu_waves_per_eu(MIN_WAVES_PER_EU)))
 sgemm_mfma_kernel(Params p)
 {
-    constexpr int NT = 64 * WAVES_M * WAVES_N;
+    constexpr int WAVES_MN = WAVES_M * WAVES_N;
+    constexpr int NT = 64 * WAVES_MN * WAVES_K;
     constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
     constexpr int TM = WM / 32, TN = WN / 32;
     static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tile must be a multiple of 32");
+    static_assert(WAVES_K == 1 || WAVES_K == 2, "WAVES_K");
     using OpA = Operand<A_KC, BM, BK, NT, VEC>;
     using OpB = Operand<B_KC, BN, BK, NT, VEC>;
 
@@ -318,8 +327,10 @@ sgemm_mfma_kernel(Params p)
     int b, tile_m, tile_n;
     tile_of(p, b, tile_m, tile_n);
     const int m0 = tile_m * BM, n0 = tile_n * BN;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm0 = (wave % WAVES_M) * WM, wn0 = (wave / WAVES_M) * WN;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wmn = wave % WAVES_MN, kgrp = wave / WAVES_MN;
+    const int wm0 = (wmn % WAVES_M) * WM, wn0 = (wmn / WAVES_M) * WN;
 
     const float *Ab = item_a(p, b), *Bb = item_b(p, b);
     float *Cb = item_c(p, b);
@@ -365,17 +376,18 @@ sgemm_mfma_kernel(Params p)
         opb.template load_next<decltype(tail)::value>(tid, rb);
     };
 
-    constexpr int NQ = BK / 8;      // groups of 8 k per K-step
-    constexpr int LATE = TM * TN;   // MFMAs of the last group issued after the barrier
+    constexpr int NQ = BK / 8 / WAVES_K; // groups of 8 k per K-step, per wave
+    constexpr int LATE = TM * TN;        // MFMAs of the last group issued after the barrier
     static_assert(NQ >= 2, "the fragment pipeline needs at least two k-groups per step");
+    const int q0 = kgrp * NQ;            // this wave's first k-group of a stage
 
     auto read_group = [&](const float *stage, int q, float (&fa)[TM][4], float (&fb)[TN][4]) {
 #pragma unroll
         for (int i = 0; i < TM; ++i)
-            OpA::frag(stage, wm0 + 32 * i, q, lane, fa[i]);
+            OpA::frag(stage, wm0 + 32 * i, q0 + q, lane, fa[i]);
 #pragma unroll
         for (int j = 0; j < TN; ++j)
-            OpB::frag(stage + OpA::STAGE, wn0 + 32 * j, q, lane, fb[j]);
+            OpB::frag(stage + OpA::STAGE, wn0 + 32 * j, q0 + q, lane, fb[j]);
     };
     // MFMA steps [first, last) of one k-group, step-major so that consecutive
     // MFMAs update different accumulators.
@@ -463,9 +475,51 @@ sgemm_mfma_kernel(Params p)
             k_step(P1{}, Tail{});
     }
 
-    // Epilogue: C = alpha * acc + beta * C, lanes outside M x N dropped.
     // Accumulator register v of lane l holds row 8*(v/4) + 4*(l/32) + v%4,
-    // column l%32 of its 32 x 32 product.
+    // column l%32 of its 32 x 32 product. With WAVES_K = 2, wave group h
+    // finishes registers [8h, 8h+8) of every tile: it receives the other
+    // group's partial sums of those through LDS and sends its own of the rest.
+    constexpr int VN = 16 / WAVES_K;     // accumulator registers finished per wave
+    const int v0 = kgrp * VN;
+    float res[TM][TN][VN];
+    if constexpr (WAVES_K == 1) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+#pragma unroll
+                for (int v = 0; v < VN; ++v)
+                    res[i][j][v] = acc[i][j][v];
+    } else {
+        static_assert(BM * BN <= 2 * STAGE, "the exchange must fit in the stages' LDS");
+        // Slot of (receiving group r, this wave's tile position, register v - 8r, lane).
+        auto xidx = [&](int r, int i, int j, int vv) {
+            return ((((r * WAVES_MN + wmn) * TM + i) * TN + j) * VN + vv) * 64 + lane;
+        };
+        __syncthreads(); // every wave is past its last read of the stages
+        const int other = 1 - kgrp;
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+#pragma unroll
+                for (int vv = 0; vv < VN; ++vv)
+                    lds[xidx(other, i, j, vv)] = kgrp == 0 ? acc[i][j][VN + vv] : acc[i][j][vv];
+        __syncthreads();
+        // Group 0's partial plus group 1's, in that order for either group
+        // (the sum of two floats does not depend on the operand order).
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+#pragma unroll
+                for (int vv = 0; vv < VN; ++vv) {
+                    const float mine = kgrp == 0 ? acc[i][j][vv] : acc[i][j][VN + vv];
+                    res[i][j][vv] = mine + lds[xidx(kgrp, i, j, vv)];
+                }
+    }
+
+    // Epilogue: C = alpha * acc + beta * C, lanes outside M x N dropped.
     const long long cbase = (long long)m0 * p.ldc + n0;
     const __amdgpu_buffer_rsrc_t rc =
         make_rsrc(Cb + cbase, (long long)(p.M - 1) * p.ldc + p.N - cbase);
@@ -477,23 +531,24 @@ sgemm_mfma_kernel(Params p)
             for (int j = 0; j < TN; ++j) {
                 const int col = wn0 + 32 * j + (lane & 31);
                 const bool col_ok = n0 + col < p.N;
-                uint32_t off[16];
-                float c[16];
+                uint32_t off[VN];
+                float c[VN];
 #pragma unroll
-                for (int v = 0; v < 16; ++v) {
+                for (int vv = 0; vv < VN; ++vv) {
+                    const int v = v0 + vv;
                     const int row = wm0 + 32 * i + 8 * (v >> 2) + 4 * g + (v & 3);
-                    off[v] = (col_ok && m0 + row < p.M)
-                                 ? (uint32_t)(((long long)row * p.ldc + col) * 4)
-                                 : kOOB;
+                    off[vv] = (col_ok && m0 + row < p.M)
+                                  ? (uint32_t)(((long long)row * p.ldc + col) * 4)
+                                  : kOOB;
                     if (with_beta)
-                        c[v] = load1(rc, off[v]);
+                        c[vv] = load1(rc, off[vv]);
                 }
 #pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    float out = p.alpha * acc[i][j][v];
+                for (int vv = 0; vv < VN; ++vv) {
+                    float out = p.alpha * res[i][j][vv];
                     if (with_beta)
-                        out += p.beta * c[v];
-                    store1(rc, off[v], out);
+                        out += p.beta * c[vv];
+                    store1(rc, off[vv], out);
                 }
             }
         }
@@ -626,13 +681,29 @@ struct DmaOperand {
 // bits 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at their maxima).
 constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
+// Wait until at most min(n, MAXN) groups of NI vector-memory operations are in
+// flight (n < 0: none). n is wave-uniform; each case has its own immediate.
+template <int NI, int MAXN>
+__device__ __forceinline__ void wait_vm_groups(int n)
+{
+    if constexpr (MAXN > 0) {
+        if (n >= MAXN) {
+            __builtin_amdgcn_s_waitcnt(waitcnt_vm(MAXN * NI));
+            return;
+        }
+        wait_vm_groups<NI, MAXN - 1>(n);
+    } else {
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    }
+}
+
 template <int WAVES, int STAGES, bool A_KC, bool B_KC, bool EVEN_K>
 __global__ void
 __attribute__((amdgpu_flat_work_group_size(64 * WAVES, 64 * WAVES), amdgpu_waves_per_eu(1)))
 sgemm_stream_kernel(Params p)
 {
     constexpr int BM = 64, BN = 64, BK = 16, TM = 2, TN = 2, NQ = BK / 8;
-    constexpr int CPT = BM * BN / (64 * WAVES); // epilogue columns per thread
+    constexpr int RPT = BM / WAVES; // epilogue rows per thread (one column per lane)
     using OpA = DmaOperand<A_KC, BM, BK>;
     using OpB = DmaOperand<B_KC, BN, BK>;
     constexpr int STAGE = OpA::FLOATS + OpB::FLOATS;      // floats per ring slot
@@ -640,8 +711,8 @@ sgemm_stream_kernel(Params p)
     constexpr int PITCH = BN + 4;                         // partial-tile row pitch
     constexpr int RING = WAVES * STAGES * STAGE;
     constexpr int PART = WAVES * BM * PITCH;
-    static_assert((STAGES - 2) * NI <= 63, "vmcnt holds at most 63");
-    static_assert(CPT % 4 == 0 && BN % CPT == 0, "epilogue split");
+    static_assert((STAGES - 2) * NI <= 63 && RPT <= 63, "vmcnt holds at most 63");
+    static_assert(BN == 64 && BM % WAVES == 0, "epilogue split");
     __shared__ __attribute__((aligned(16))) float lds[RING > PART ? RING : PART];
 
     int b, tile_m, tile_n;
@@ -677,9 +748,7 @@ sgemm_stream_kernel(Params p)
     opb.init(lane, wave * BK, WAVES * BK);
 
     float *ring = lds + wave * STAGES * STAGE;
-    // My j-th step is K-step wave + 4 j. Steps past K load zeros (or unused
-    // in-range data) into slots that are never read, which keeps the number
-    // of outstanding loads, and so every vmcnt wait, a constant.
+    // My j-th step is K-step wave + WAVES j; its loads go to ring slot j % STAGES.
     auto issue = [&](int j) {
         float *slot = ring + (j % STAGES) * STAGE;
         opa.template issue<!EVEN_K>(slot, lane);
@@ -706,37 +775,63 @@ sgemm_stream_kernel(Params p)
         for (int t = 0; t < TN; ++t)
             acc[i][t] = f32x16{};
 
+    // Loads run STAGES - 1 steps ahead of the MFMAs and stop at the wave's
+    // last step; waiting for step s leaves the loads of the steps issued after
+    // it in flight (vector-memory operations complete in issue order).
     const int nsteps = (p.K + BK - 1) / BK;
     const int mine = wave < nsteps ? (nsteps - wave + WAVES - 1) / WAVES : 0;
 #pragma unroll
     for (int j = 0; j < STAGES - 1; ++j)
-        issue(j);
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm((STAGES - 2) * NI));
+        if (j < mine)
+            issue(j);
+    wait_vm_groups<NI, STAGES - 2>(mine - 1);
     read(0, fa[0], fb[0]);
-    for (int j = 0; j < mine; j += 2) {
-        // Two steps per trip so the register double buffer has static indices.
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            if (h == 1 && j + 1 >= mine)
-                break;
-            issue(j + h + STAGES - 1);
+    // Step i: issue step i + STAGES - 1 (if it exists), wait for step i + 1,
+    // read it into the other register buffer, multiply step i. H is i's
+    // parity, so the register double buffer has static indices.
+    auto step = [&](auto h, auto steady, int i) {
+        constexpr int H = decltype(h)::value;
+        if (decltype(steady)::value) {
+            issue(i + STAGES - 1);
             __builtin_amdgcn_s_waitcnt(waitcnt_vm((STAGES - 2) * NI));
-            read(j + h + 1, fa[h ^ 1], fb[h ^ 1]);
-#pragma unroll
-            for (int q = 0; q < NQ; ++q)
-#pragma unroll
-                for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-                    for (int i = 0; i < TM; ++i)
-#pragma unroll
-                        for (int t = 0; t < TN; ++t)
-                            acc[i][t] = __builtin_amdgcn_mfma_f32_32x32x2f32(
-                                fa[h][q][i][kk], fb[h][q][t][kk], acc[i][t], 0, 0, 0);
+        } else if (i + STAGES - 1 < mine) {
+            issue(i + STAGES - 1);
+            __builtin_amdgcn_s_waitcnt(waitcnt_vm((STAGES - 2) * NI));
+        } else {
+            wait_vm_groups<NI, STAGES - 2>(mine - 2 - i); // steps issued after i + 1
         }
+        // (After the last step this reads a slot whose values are unused.)
+        read(i + 1, fa[H ^ 1], fb[H ^ 1]);
+#pragma unroll
+        for (int q = 0; q < NQ; ++q)
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+                for (int ii = 0; ii < TM; ++ii)
+#pragma unroll
+                    for (int t = 0; t < TN; ++t)
+                        acc[ii][t] = __builtin_amdgcn_mfma_f32_32x32x2f32(
+                            fa[H][q][ii][kk], fb[H][q][t][kk], acc[ii][t], 0, 0, 0);
+    };
+    using H0 = std::integral_constant<int, 0>;
+    using H1 = std::integral_constant<int, 1>;
+    // Steady state: every step issues a load and waits a fixed count; one
+    // basic block per trip, so the loads interleave with the MFMAs.
+    const int steady_end = mine - (STAGES - 1);
+    int i = 0;
+    for (; i + 1 < steady_end; i += 2) {
+        step(H0{}, std::true_type{}, i);
+        step(H1{}, std::true_type{}, i + 1);
+    }
+    // The last steps (i is even here).
+    for (; i < mine; i += 2) {
+        step(H0{}, std::false_type{}, i);
+        if (i + 1 < mine)
+            step(H1{}, std::false_type{}, i + 1);
     }
 
-    // Sum the four partial tiles in a fixed order and apply the epilogue.
-    __builtin_amdgcn_s_waitcnt(0);
+    // Sum the partial tiles of the waves in a fixed order (wave 0's first).
+    // The loop above has already waited for all of this wave's ring loads.
     __syncthreads();
     float *part = lds + wave * BM * PITCH;
     const int g = lane >> 5;
@@ -748,44 +843,37 @@ sgemm_stream_kernel(Params p)
             for (int v = 0; v < 16; ++v)
                 part[(32 * i + 8 * (v >> 2) + 4 * g + (v & 3)) * PITCH + 32 * t + (lane & 31)] =
                     acc[i][t][v];
-    __syncthreads();
-    const int row = (int)threadIdx.x / (BN / CPT), col0 = ((int)threadIdx.x % (BN / CPT)) * CPT;
-    float sum[CPT];
-#pragma unroll
-    for (int c = 0; c < CPT; c += 4) {
-        f32x4 x = *reinterpret_cast<const f32x4 *>(lds + row * PITCH + col0 + c);
-#pragma unroll
-        for (int w = 1; w < WAVES; ++w) {
-            const f32x4 y =
-                *reinterpret_cast<const f32x4 *>(lds + (w * BM + row) * PITCH + col0 + c);
-            x += y;
-        }
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-            sum[c + e] = x[e];
-    }
+
+    // Epilogue: thread (wave, lane) finishes column `lane` of rows wave + WAVES*r,
+    // so every C access of a wave is one contiguous row. With beta != 0 the C
+    // loads are issued before the barrier and land while the partials are summed.
     const long long cbase = (long long)m0 * p.ldc + n0;
     const __amdgpu_buffer_rsrc_t rc =
         make_rsrc(Cb + cbase, (long long)(p.M - 1) * p.ldc + p.N - cbase);
-    const bool row_ok = m0 + row < p.M;
-    uint32_t off[CPT];
+    const bool col_ok = n0 + lane < p.N;
+    uint32_t off[RPT];
 #pragma unroll
-    for (int c = 0; c < CPT; ++c)
-        off[c] = (row_ok && n0 + col0 + c < p.N)
-                     ? (uint32_t)(((long long)row * p.ldc + col0 + c) * 4)
-                     : kOOB;
-    if (p.beta != 0.0f) {
-        float cin[CPT];
+    for (int r = 0; r < RPT; ++r) {
+        const int row = wave + WAVES * r;
+        off[r] = (col_ok && m0 + row < p.M) ? (uint32_t)(((long long)row * p.ldc + lane) * 4)
+                                            : kOOB;
+    }
+    const bool with_beta = p.beta != 0.0f;
+    float cin[RPT];
+    if (with_beta) {
 #pragma unroll
-        for (int c = 0; c < CPT; ++c)
-            cin[c] = load1(rc, off[c]);
+        for (int r = 0; r < RPT; ++r)
+            cin[r] = load1(rc, off[r]);
+    }
+    __syncthreads();
 #pragma unroll
-        for (int c = 0; c < CPT; ++c)
-            store1(rc, off[c], p.alpha * sum[c] + p.beta * cin[c]);
-    } else {
+    for (int r = 0; r < RPT; ++r) {
+        const int row = wave + WAVES * r;
+        float x = lds[row * PITCH + lane];
 #pragma unroll
-        for (int c = 0; c < CPT; ++c)
-            store1(rc, off[c], p.alpha * sum[c]);
+        for (int w = 1; w < WAVES; ++w)
+            x += lds[(w * BM + row) * PITCH + lane];
+        store1(rc, off[r], with_beta ? p.alpha * x + p.beta * cin[r] : p.alpha * x);
     }
 }
 
@@ -811,31 +899,31 @@ __global__ void __launch_bounds__(256) sgemm_scale_kernel(float *C, float *const
 typedef void (*KernelFn)(Params);
 
 struct VariantInfo {
-    int bm, bn, threads, vec;
+    int bm, bn, bk, threads, vec;
     KernelFn fn[2][2][2]; // [transA][transB][even_k]
 };
 
-template <int BM, int BN, int BK, int WM_, int WN_, int MW, int VEC>
+constexpr int kBK = 16;
+
+template <int BM, int BN, int BK, int WM_, int WN_, int WK_, int MW, int VEC>
 constexpr VariantInfo make_variant()
 {
     return VariantInfo{
-        BM, BN, 64 * WM_ * WN_, VEC,
-        {{{sgemm_mfma_kernel<BM, BN, BK, WM_, WN_, MW, true, false, false, VEC>,
-           sgemm_mfma_kernel<BM, BN, BK, WM_, WN_, MW, true, false, true, VEC>},
-          {sgemm_mfma_kernel<BM, BN, BK, WM_, WN_, MW, true, true, false, VEC>,
-           sgemm_mfma_kernel<BM, BN, BK, WM_, WN_, MW, true, true, true, VEC>}},
-         {{sgemm_mfma_kernel<BM, BN, BK, WM_, WN_, MW, false, false, false, VEC>,
-           sgemm_mfma_kernel<BM, BN, BK, WM_, WN_, MW, false, false, true, VEC>},
-          {sgemm_mfma_kernel<BM, BN, BK, WM_, WN_, MW, false, true, false, VEC>,
-           sgemm_mfma_kernel<BM, BN, BK, WM_, WN_, MW, false, true, true, VEC>}}}};
+        BM, BN, BK, 64 * WM_ * WN_ * WK_, VEC,
+        {{{sgemm_mfma_kernel<BM, BN, BK, WM_, WN_, WK_, MW, true, false, false, VEC>,
+           sgemm_mfma_kernel<BM, BN, BK, WM_, WN_, WK_, MW, true, false, true, VEC>},
+          {sgemm_mfma_kernel<BM, BN, BK, WM_, WN_, WK_, MW, true, true, false, VEC>,
+           sgemm_mfma_kernel<BM, BN, BK, WM_, WN_, WK_, MW, true, true, true, VEC>}},
+         {{sgemm_mfma_kernel<BM, BN, BK, WM_, WN_, WK_, MW, false, false, false, VEC>,
+           sgemm_mfma_kernel<BM, BN, BK, WM_, WN_, WK_, MW, false, false, true, VEC>},
+          {sgemm_mfma_kernel<BM, BN, BK, WM_, WN_, WK_, MW, false, true, false, VEC>,
+           sgemm_mfma_kernel<BM, BN, BK, WM_, WN_, WK_, MW, false, true, true, VEC>}}}};
 }
-
-constexpr int kBK = 16;
 
 template <int WAVES, int STAGES>
 constexpr VariantInfo make_stream_variant()
 {
-    return VariantInfo{64, 64, 64 * WAVES, 4,
+    return VariantInfo{64, 64, 16, 64 * WAVES, 4,
                        {{{sgemm_stream_kernel<WAVES, STAGES, true, false, false>,
                           sgemm_stream_kernel<WAVES, STAGES, true, false, true>},
                          {sgemm_stream_kernel<WAVES, STAGES, true, true, false>,
@@ -847,12 +935,13 @@ constexpr VariantInfo make_stream_variant()
 }
 
 const VariantInfo kVariants[SGEMM_VARIANT_COUNT] = {
-    make_variant<256, 128, kBK, 2, 2, 2, 4>(), // SGEMM_VARIANT_L256x128
-    make_variant<128, 128, kBK, 2, 2, 2, 4>(), // SGEMM_VARIANT_M128x128
-    make_variant<64, 64, kBK, 2, 2, 4, 4>(),   // SGEMM_VARIANT_S64x64
-    make_variant<64, 64, kBK, 2, 2, 4, 1>(),   // SGEMM_VARIANT_S64x64_V1
-    make_stream_variant<4, 4>(),               // SGEMM_VARIANT_T64x64
-    make_variant<256, 256, kBK, 2, 4, 2, 4>(), // SGEMM_VARIANT_L256x256
+    make_variant<256, 128, kBK, 2, 2, 1, 2, 4>(), // SGEMM_VARIANT_L256x128
+    make_variant<128, 128, kBK, 2, 2, 1, 2, 4>(), // SGEMM_VARIANT_M128x128
+    make_variant<64, 64, kBK, 2, 2, 1, 4, 4>(),   // SGEMM_VARIANT_S64x64
+    make_variant<64, 64, kBK, 2, 2, 1, 4, 1>(),   // SGEMM_VARIANT_S64x64_V1
+    make_stream_variant<4, 4>(),                  // SGEMM_VARIANT_T64x64
+    make_variant<256, 256, kBK, 2, 4, 1, 2, 4>(), // SGEMM_VARIANT_L256x256
+    make_variant<64, 64, 32, 2, 2, 2, 2, 4>(),    // SGEMM_VARIANT_S64x64_K2
 };
 
 long long ceil_div(long long a, long long b) { return (a + b - 1) / b; }
@@ -926,15 +1015,24 @@ extern "C" int sgemm_select_variant(int transA, int transB, int M, int N, int K,
         num_cus = 1;
     const long long cus = num_cus;
     const long long tiles256 = ceil_div(M, 256) * ceil_div(N, 256) * batch;
-    // One skinny dimension over a deep K: stream the long operand through
-    // per-wave LDS rings, four waves splitting each 64 x 64 tile's K.
-    if ((M <= 64 || N <= 64) && K >= 512 && ceil_div(M, 64) * ceil_div(N, 64) * batch <= 2 * cus)
+    const long long tiles64 = ceil_div(M, 64) * ceil_div(N, 64) * batch;
+    // One skinny dimension over a deep K, with the long operand stored
+    // k-contiguous (A with transA = 0 when N is skinny, B with transB = 1 when
+    // M is): stream it through per-wave LDS rings, four waves splitting each
+    // 64 x 64 tile's K.
+    const bool long_kc = N <= 64 ? transA == 0 : transB == 1;
+    if ((M <= 64 || N <= 64) && long_kc && K >= 512 && tiles64 <= 2 * cus)
         return SGEMM_VARIANT_T64x64;
     // Exactly one wave of 256 x 256 tiles over a deep K: the eight-wave
     // workgroup (two waves per SIMD in step) edges out two 256 x 128
     // workgroups per CU.
     if (K >= 2048 && tiles256 <= cus && 10 * tiles256 >= 9 * cus)
         return SGEMM_VARIANT_L256x256;
+    // Few 64 x 64 tiles per CU (up to 9) over K >= 768: the eight-wave 64 x 64
+    // tile whose two wave groups split every K-step keeps two waves on each
+    // SIMD, where the larger tiles would leave CUs idle or under-occupied.
+    if (K >= 768 && tiles64 <= 9 * cus)
+        return SGEMM_VARIANT_S64x64_K2;
     // Otherwise the tile whose busiest CU finishes first: a CU receives
     // ceil(tiles / CUs) tiles, each costing its area over the variant's
     // relative efficiency (smaller tiles reuse each loaded byte less).
@@ -1013,7 +1111,7 @@ int launch(const Call &c, int variant, hipStream_t s)
     }
 
     const VariantInfo &vi = kVariants[variant];
-    const int even_k = c.K % kBK == 0 ? 1 : 0;
+    const int even_k = c.K % vi.bk == 0 ? 1 : 0;
     Params p;
     p.A = c.A;
     p.B = c.B;

@@ -35,6 +35,18 @@ def test_header_declares_the_entry_points():
         assert n in names
 
 
+def test_binding_mirrors_the_variant_enum(pg):
+    """The binding's variant constants match the header's enum."""
+    text = open(HEADER).read()
+    enum = dict((n, int(v)) for n, v in re.findall(r"SGEMM_VARIANT_(\w+)\s*=\s*(-?\d+)", text))
+    assert enum["COUNT"] == pg.VARIANT_COUNT == len(pg.VARIANT_NAMES)
+    for name, value in enum.items():
+        if name != "COUNT":
+            assert getattr(pg, "VARIANT_" + name) == value, name
+            if value >= 0:
+                assert pg.VARIANT_NAMES[value] == name
+
+
 def test_library_exports_every_declared_symbol(pg):
     out = subprocess.run(["nm", "-D", "--defined-only", pg.library_path()],
                          capture_output=True, text=True, check=True).stdout
@@ -98,7 +110,7 @@ def test_quick_returns_launch_nothing(pg, over):
 def test_variant_argument_checked(pg):
     a = base_args()
     st = pg.sgemm_strided_batched_variant(0, 0, 4, 4, 4, 1.0, FAKE, 4, FAKE, 4, 0.0, FAKE, 4,
-                                          1, 0, 0, 0, 7, check=False)
+                                          1, 0, 0, 0, pg.VARIANT_COUNT, check=False)
     assert st == -18
     st = pg.sgemm_strided_batched_variant(0, 0, 4, 4, 4, 1.0, FAKE + 4, 4, FAKE, 4, 0.0, FAKE,
                                           4, 1, 0, 0, 0, pg.VARIANT_S64x64, check=False)
@@ -120,16 +132,22 @@ def test_select_variant(pg):
     assert sel(1, 0, 512, 512, 520, 64, True, 256) == pg.VARIANT_L256x128
     # 8192^3: eight 256 x 128 tiles per CU beat sixteen 128 x 128 ones
     assert sel(0, 0, 8192, 8192, 8192, 1, True, 256) == pg.VARIANT_L256x128
-    # 2048^3 and 6144^3: 128 x 128 tiles spread evenly over the CUs
-    assert sel(0, 0, 2048, 2048, 2048, 1, True, 256) == pg.VARIANT_M128x128
+    # 6144^3: 128 x 128 tiles spread evenly over the CUs (nine per CU)
     assert sel(0, 0, 6144, 6144, 6144, 1, True, 256) == pg.VARIANT_M128x128
-    # 3072^3: 2304 tiles of 64 x 64 are nine per CU, 128 x 128 tiles are 2.25
-    assert sel(0, 0, 3072, 3072, 3072, 1, True, 256) == pg.VARIANT_S64x64
-    # 1024^3: 64 x 64 tiles, one per CU
-    assert sel(0, 0, 1024, 1024, 1024, 1, True, 256) == pg.VARIANT_S64x64
-    # skinny shapes stream
+    # up to nine 64 x 64 tiles per CU over K >= 768: the K-split eight-wave tile
+    for shape in ((1024, 1024, 1024), (2048, 2048, 2048), (3072, 3072, 3072),
+                  (1024, 1024, 4096), (1000, 1000, 1000), (64, 8192, 8192)):
+        assert sel(0, 0, *shape, 1, True, 256) == pg.VARIANT_S64x64_K2, shape
+    assert sel(0, 0, 512, 512, 2048, 8, True, 256) == pg.VARIANT_S64x64_K2
+    # ... but not over a short K, nor past nine tiles per CU
+    assert sel(0, 0, 2048, 2048, 512, 1, True, 256) == pg.VARIANT_M128x128
+    assert sel(0, 0, 512, 512, 512, 1, True, 256) == pg.VARIANT_S64x64
+    assert sel(0, 0, 3136, 3136, 3136, 1, True, 256) != pg.VARIANT_S64x64_K2
+    # skinny shapes whose long operand is k-contiguous stream
     assert sel(0, 1, 16384, 64, 4096, 1, True, 256) == pg.VARIANT_T64x64
-    assert sel(0, 0, 64, 8192, 8192, 1, True, 256) == pg.VARIANT_T64x64
+    assert sel(0, 0, 16384, 64, 4096, 1, True, 256) == pg.VARIANT_T64x64
+    assert sel(0, 1, 64, 8192, 8192, 1, True, 256) == pg.VARIANT_T64x64
+    assert sel(1, 1, 16384, 64, 4096, 1, True, 256) != pg.VARIANT_T64x64
     assert sel(0, 1, 16384, 64, 128, 1, True, 256) != pg.VARIANT_T64x64
     # no 4-float loads: the 1-float variant
     assert sel(0, 0, 4092, 4092, 4092, 1, False, 256) == pg.VARIANT_S64x64_V1

@@ -17,10 +17,14 @@ import numpy as np
 import pytest
 
 import oracle
+import precision_gemm_amd as pg_constants  # module constants only; the library loads in env()
 import workloads
 from workloads import Workload
 
 pytestmark = pytest.mark.gpu
+
+# every kernel variant (the enum of the C header, mirrored by the binding)
+ALL_VARIANTS = list(range(pg_constants.VARIANT_COUNT))
 
 GUARD = 64  # floats of canary before and after each device buffer (keeps 256-B alignment)
 
@@ -170,7 +174,7 @@ SIZES4 = [4, 8, 12, 16, 20, 28, 32, 36, 60, 64, 68, 124, 128, 132, 252, 256, 260
 def sweep_shapes(n, seed):
     rng = np.random.default_rng(seed)
     shapes = {(1, 1, 1), (4, 4, 4), (257, 257, 257), (256, 128, 16), (255, 129, 33),
-              (260, 132, 20)}
+              (260, 132, 20), (132, 68, 64), (68, 196, 96), (200, 72, 48)}
     while len(shapes) < n:
         pool = SIZES4 if len(shapes) % 2 else SIZES
         shapes.add(tuple(int(x) for x in rng.choice(pool, 3)))
@@ -184,7 +188,7 @@ def vec4_possible(w):
            w.LDA % 4 == 0 and w.LDB % 4 == 0 and w.SA % 4 == 0 and w.SB % 4 == 0
 
 
-@pytest.mark.parametrize("variant", [0, 1, 2, 3, 4, 5])
+@pytest.mark.parametrize("variant", ALL_VARIANTS)
 def test_integer_sweep_bitwise(env, variant):
     """Every forced variant x transpose pair over ragged sizes, integer inputs:
     bitwise equality with the oracle."""
@@ -211,7 +215,7 @@ def test_integer_sweep_bitwise(env, variant):
     assert n_run > 20
 
 
-@pytest.mark.parametrize("variant", [0, 1, 2, 3, 4, 5])
+@pytest.mark.parametrize("variant", ALL_VARIANTS)
 def test_float_sweep_bound(env, variant):
     """Random fp32 inputs, several tiles plus ragged tails in every dimension,
     all transposes, padded leading dimensions, batches with gaps."""
@@ -278,7 +282,7 @@ def test_broadcast_and_strided_batches(env):
     w = Workload("bcast", 0, 1, 200, 136, 96, 1.0, 0.5, seed=9, batch=5,
                  stride_a=0, stride_b=136 * 96 + 12, stride_c=200 * 136 + 36)
     A, B, C = workloads.make_inputs(w)
-    for variant in (-1, 0, 1, 2, 3, 4, 5):
+    for variant in (-1, *ALL_VARIANTS):
         st, got = run_gpu(env, w, A, B, C, variant=variant)
         assert st == 0
         check_against_oracle(w, A, B, C, got)
@@ -364,7 +368,7 @@ def test_batch_offsets_beyond_2_pow_31_elements(env):
     dB = torch.from_numpy(Bm.reshape(-1)).to(dev)
     dC = torch.from_numpy(Cm.reshape(-1)).to(dev)
     log(f"[extreme] strideA={stride}")
-    for variant in (-1, 0, 2, 4):
+    for variant in (-1, 0, 2, 4, 6):
         dC.copy_(torch.from_numpy(Cm.reshape(-1)))
         st = pg.sgemm_strided_batched_variant(0, 0, M, N, K, 1.0, big, K, dB, N, 2.0, dC, N, 2,
                                               stride, K * N, M * N, variant, check=False)
@@ -457,7 +461,7 @@ def check_items(tA, tB, M, N, K, alpha, beta, lda, ldb, ldc, res, exact):
         check_against_oracle(w, A, B, C, got, exact=exact)
 
 
-@pytest.mark.parametrize("variant", [-1, 0, 1, 2, 3, 4, 5])
+@pytest.mark.parametrize("variant", [-1, *ALL_VARIANTS])
 def test_pointer_array_bitwise(env, variant):
     """Pointer-array batches on every variant and transpose pair, integer
     inputs: bitwise equal to the oracle run item by item, with a shared A
@@ -473,7 +477,7 @@ def test_pointer_array_bitwise(env, variant):
         check_items(tA, tB, M, N, K, 2.0, -1.0, lda, ldb, ldc, res, exact=True)
 
 
-@pytest.mark.parametrize("variant", [-1, 0, 2, 4, 5])
+@pytest.mark.parametrize("variant", [-1, 0, 2, 4, 5, 6])
 def test_pointer_array_misaligned_items(env, variant):
     """Items whose A or B is not 16-byte aligned, in a launch of a 4-float
     kernel: those items take the kernel's plain per-element path and must
