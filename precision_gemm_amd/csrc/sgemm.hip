@@ -1014,35 +1014,31 @@ extern "C" int sgemm_select_variant(int transA, int transB, int M, int N, int K,
     if (num_cus < 1)
         num_cus = 1;
     const long long cus = num_cus;
-    const long long tiles256 = ceil_div(M, 256) * ceil_div(N, 256) * batch;
     const long long tiles64 = ceil_div(M, 64) * ceil_div(N, 64) * batch;
-    // One skinny dimension over a deep K, with the long operand stored
-    // k-contiguous (A with transA = 0 when N is skinny, B with transB = 1 when
-    // M is): stream it through per-wave LDS rings, four waves splitting each
-    // 64 x 64 tile's K.
-    const bool long_kc = N <= 64 ? transA == 0 : transB == 1;
-    if ((M <= 64 || N <= 64) && long_kc && K >= 512 && tiles64 <= 2 * cus)
+    // One skinny dimension (<= 64) over a deep K whose long operand is too
+    // large to stay in the 256 MB Infinity Cache from one call to the next
+    // (over 128 MiB): the streaming kernel, whose per-wave rings keep the most
+    // bytes in flight while that operand streams from HBM. A smaller long
+    // operand stays cached, and the tiles below do better on it.
+    const long long long_bytes = 4LL * (M > N ? M : N) * K * batch;
+    if ((M <= 64 || N <= 64) && K >= 512 && tiles64 <= 2 * cus && long_bytes > (128LL << 20))
         return SGEMM_VARIANT_T64x64;
-    // Exactly one wave of 256 x 256 tiles over a deep K: the eight-wave
-    // workgroup (two waves per SIMD in step) edges out two 256 x 128
-    // workgroups per CU.
-    if (K >= 2048 && tiles256 <= cus && 10 * tiles256 >= 9 * cus)
-        return SGEMM_VARIANT_L256x256;
-    // Few 64 x 64 tiles per CU (up to 9) over K >= 768: the eight-wave 64 x 64
-    // tile whose two wave groups split every K-step keeps two waves on each
-    // SIMD, where the larger tiles would leave CUs idle or under-occupied.
-    if (K >= 768 && tiles64 <= 9 * cus)
-        return SGEMM_VARIANT_S64x64_K2;
     // Otherwise the tile whose busiest CU finishes first: a CU receives
     // ceil(tiles / CUs) tiles, each costing its area over the variant's
-    // relative efficiency (smaller tiles reuse each loaded byte less).
-    struct Choice { int variant, bm, bn, eff_pct; };
-    const Choice choices[] = {{SGEMM_VARIANT_L256x128, 256, 128, 100},
-                              {SGEMM_VARIANT_M128x128, 128, 128, 97},
-                              {SGEMM_VARIANT_S64x64, 64, 64, 92}};
+    // relative efficiency. The efficiencies are fitted to a sweep of every
+    // variant over 24 shapes (precision_gemm_amd/tune.py): 128 x 128 tiles
+    // 1.00; the K-split 64 x 64 tile 0.88, for K >= 768; plain 64 x 64 tiles
+    // 0.85. The 256-row tiles never won by more than the sweep's noise, so
+    // they are left to explicit requests.
+    struct Choice { int variant, bm, bn, eff_pct; long long min_k; };
+    const Choice choices[] = {{SGEMM_VARIANT_M128x128, 128, 128, 100, 0},
+                              {SGEMM_VARIANT_S64x64_K2, 64, 64, 88, 768},
+                              {SGEMM_VARIANT_S64x64, 64, 64, 85, 0}};
     int best = SGEMM_VARIANT_S64x64;
     double best_cost = -1.0;
     for (const Choice &c : choices) {
+        if (K < c.min_k)
+            continue;
         const long long tiles = ceil_div(M, c.bm) * ceil_div(N, c.bn) * batch;
         const double cost = (double)ceil_div(tiles, cus) * c.bm * c.bn * 100.0 / c.eff_pct;
         if (best_cost < 0 || cost < best_cost) {

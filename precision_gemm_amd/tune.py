@@ -1,0 +1,159 @@
+"""Dispatch sweep: time every kernel variant on a grid of shapes and report how
+far the library's automatic choice is from the fastest one.
+
+    python -m precision_gemm_amd.tune [--shapes default|quick] [--json out.json]
+
+For each shape every applicable variant is timed on the same device buffers,
+interleaved over several rounds (so clock drift hits all variants alike); a
+variant's time is the median of its rounds, each round the mean of
+back-to-back launches between two HIP events on the launch stream, preceded by
+an untimed window of the same variant.
+The report lists the fastest variant, the one `sgemm_select_variant` picks and
+the regret (automatic time / fastest time - 1). The cost model in the host
+dispatcher is fitted to these tables.
+
+Inputs are U(-1, 1) fp32 from a fixed seed. Only whether beta is zero changes
+the work (C is read iff beta != 0), so a nonzero beta is timed as 1.0, which
+keeps C bounded over the repeated launches (C is not restored between them).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import statistics
+import sys
+import time
+
+# (transA, transB, M, N, K, batch, beta)
+DEFAULT_SHAPES = [
+    (0, 0, 128, 128, 128, 1, 0.0),
+    (0, 0, 512, 512, 512, 1, 0.0),
+    (0, 0, 768, 768, 768, 1, 0.0),
+    (0, 0, 1024, 1024, 1024, 1, 3.0),
+    (1, 1, 1000, 1000, 1000, 1, 1.0),
+    (0, 0, 1536, 1536, 1536, 1, 0.0),
+    (0, 0, 2048, 2048, 2048, 1, 0.0),
+    (0, 0, 2048, 2048, 512, 1, 0.0),
+    (0, 0, 2560, 2560, 2560, 1, 0.0),
+    (0, 0, 3072, 3072, 3072, 1, 0.0),
+    (0, 0, 4092, 4092, 4092, 1, 0.5),
+    (0, 0, 4096, 4096, 1024, 1, 0.0),
+    (0, 0, 6144, 6144, 6144, 1, 0.0),
+    (0, 0, 8192, 8192, 8192, 1, 0.0),
+    (0, 0, 1024, 1024, 4096, 1, 0.0),
+    (0, 0, 512, 512, 8192, 1, 0.0),
+    (1, 0, 512, 512, 520, 64, 0.0),
+    (0, 0, 256, 256, 256, 128, 0.0),
+    (0, 0, 512, 512, 2048, 8, 0.0),
+    (0, 1, 16384, 64, 4096, 1, 1.0),
+    (0, 1, 16384, 64, 2048, 1, 1.0),
+    (0, 1, 64, 8192, 4096, 1, 0.0),
+    (0, 0, 16384, 64, 4096, 1, 0.0),
+    (1, 1, 16384, 64, 4096, 1, 0.0),
+]
+QUICK_SHAPES = [DEFAULT_SHAPES[i] for i in (3, 6, 10, 16, 19)]
+
+
+def time_variant(torch, pg, stream, call, launches: int) -> float:
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(launches):
+        call()
+    e1.record(stream)
+    e1.synchronize()
+    return e0.elapsed_time(e1) / launches * 1e3  # microseconds
+
+
+def sweep(shapes, rounds: int = 3, target_ms: float = 20.0, out=sys.stdout):
+    import torch
+
+    import precision_gemm_amd as pg
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    gen = torch.Generator(device=dev).manual_seed(1234)
+
+    # Let the clock ramp up before the first measurement.
+    X = torch.rand(4096, 4096, device=dev, generator=gen)
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < 0.4:
+        pg.sgemm(0, 0, 4096, 4096, 4096, 1.0, X, 4096, X, 4096, 0.0, X, 4096)
+        torch.cuda.synchronize(dev)
+    del X
+
+    results = []
+    for tA, tB, M, N, K, batch, beta in shapes:
+        beta_t = 1.0 if beta != 0.0 else 0.0
+
+        def buf(rows, cols):
+            return torch.rand((batch, rows, cols), device=dev, generator=gen) * 2 - 1
+        A = buf(K, M) if tA else buf(M, K)
+        B = buf(N, K) if tB else buf(K, N)
+        C = buf(M, N)
+        lda, ldb = A.shape[2], B.shape[2]
+        sa, sb, sc = A.stride(0), B.stride(0), C.stride(0)
+        auto = pg.sgemm_select_variant(tA, tB, M, N, K, batch, 1, cus)
+        variants = [v for v in range(pg.VARIANT_COUNT) if v != pg.VARIANT_S64x64_V1]
+
+        def caller(v):
+            return lambda: pg.sgemm_strided_batched_variant(
+                tA, tB, M, N, K, 1.0, A, lda, B, ldb, beta_t, C, N, batch, sa, sb, sc, v,
+                stream=stream.cuda_stream)
+        calls = {v: caller(v) for v in variants}
+        launches = {}
+        for v, call in calls.items():
+            for _ in range(2):
+                call()
+            torch.cuda.synchronize(dev)
+            one = time_variant(torch, pg, stream, call, 3)
+            launches[v] = max(3, min(500, int(target_ms * 1e3 / max(one, 1.0))))
+        # Each timed window follows an untimed one of the same variant: the
+        # clock settles differently after an under-filled grid (a large tile
+        # on a small problem leaves most CUs idle) and needs a few ms to
+        # return to the level the variant itself sustains.
+        times = {v: [] for v in variants}
+        for _ in range(rounds):
+            for v in variants:
+                time_variant(torch, pg, stream, calls[v], max(2, launches[v] // 2))
+                times[v].append(time_variant(torch, pg, stream, calls[v], launches[v]))
+        med = {v: statistics.median(ts) for v, ts in times.items()}
+        best = min(med, key=med.get)
+        flops = 2.0 * M * N * K * batch
+        row = {
+            "shape": {"transA": tA, "transB": tB, "M": M, "N": N, "K": K, "batch": batch,
+                      "beta": beta},
+            "us": {pg.VARIANT_NAMES[v]: round(t, 2) for v, t in med.items()},
+            "best": pg.VARIANT_NAMES[best],
+            "auto": pg.VARIANT_NAMES[auto],
+            "auto_tflops": round(flops / med[auto] / 1e6, 1),
+            "regret": round(med[auto] / med[best] - 1.0, 4),
+        }
+        results.append(row)
+        print(f"{'NT'[tA]}{'NT'[tB]} {M}x{N}x{K} b{batch} beta {beta}: best {row['best']} "
+              f"{med[best]:.1f} us, auto {row['auto']} {med[auto]:.1f} us "
+              f"({row['auto_tflops']} TFLOP/s), regret {100 * row['regret']:.1f} %  | " +
+              " ".join(f"{pg.VARIANT_NAMES[v]}={t:.1f}" for v, t in med.items()),
+              file=out, flush=True)
+    return results
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--shapes", choices=["default", "quick"], default="default")
+    ap.add_argument("--rounds", type=int, default=3)
+    ap.add_argument("--json", default=None, help="write the table as JSON here")
+    args = ap.parse_args(argv)
+    shapes = DEFAULT_SHAPES if args.shapes == "default" else QUICK_SHAPES
+    res = sweep(shapes, rounds=args.rounds)
+    regrets = [r["regret"] for r in res]
+    print(f"shapes {len(res)}: mean regret {100 * statistics.mean(regrets):.2f} %, "
+          f"max {100 * max(regrets):.2f} %", flush=True)
+    if args.json:
+        with open(args.json, "w") as f:
+            json.dump(res, f, indent=1)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

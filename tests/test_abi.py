@@ -126,29 +126,30 @@ def test_status_strings(pg):
 
 def test_select_variant(pg):
     sel = pg.sgemm_select_variant
-    # 4092^3: one wave of 16 x 16 tiles of 256 x 256 on 256 CUs
-    assert sel(0, 0, 4092, 4092, 4092, 1, True, 256) == pg.VARIANT_L256x256
-    # batched 64 x 512^2: 512 tiles of 256 x 128 = two per CU
-    assert sel(1, 0, 512, 512, 520, 64, True, 256) == pg.VARIANT_L256x128
-    # 8192^3: eight 256 x 128 tiles per CU beat sixteen 128 x 128 ones
-    assert sel(0, 0, 8192, 8192, 8192, 1, True, 256) == pg.VARIANT_L256x128
-    # 6144^3: 128 x 128 tiles spread evenly over the CUs (nine per CU)
-    assert sel(0, 0, 6144, 6144, 6144, 1, True, 256) == pg.VARIANT_M128x128
-    # up to nine 64 x 64 tiles per CU over K >= 768: the K-split eight-wave tile
-    for shape in ((1024, 1024, 1024), (2048, 2048, 2048), (3072, 3072, 3072),
-                  (1024, 1024, 4096), (1000, 1000, 1000), (64, 8192, 8192)):
+    # whole waves of 128 x 128 tiles: 4092^3 (1024 tiles, four per CU), 2048^3,
+    # 6144^3, 8192^3 and the batched 64 x 512^2 workload
+    for shape, batch, tA in (((4092, 4092, 4092), 1, 0), ((2048, 2048, 2048), 1, 0),
+                             ((6144, 6144, 6144), 1, 0), ((8192, 8192, 8192), 1, 0),
+                             ((512, 512, 520), 64, 1), ((2048, 2048, 512), 1, 0)):
+        assert sel(tA, 0, *shape, batch, True, 256) == pg.VARIANT_M128x128, shape
+    # few 64 x 64 tiles per CU over K >= 768: the K-split eight-wave tile
+    for shape in ((1024, 1024, 1024), (3072, 3072, 3072), (1536, 1536, 1536),
+                  (1024, 1024, 4096), (1000, 1000, 1000), (512, 512, 8192)):
         assert sel(0, 0, *shape, 1, True, 256) == pg.VARIANT_S64x64_K2, shape
     assert sel(0, 0, 512, 512, 2048, 8, True, 256) == pg.VARIANT_S64x64_K2
-    # ... but not over a short K, nor past nine tiles per CU
-    assert sel(0, 0, 2048, 2048, 512, 1, True, 256) == pg.VARIANT_M128x128
+    # ... and the plain 64 x 64 tile below K = 768
     assert sel(0, 0, 512, 512, 512, 1, True, 256) == pg.VARIANT_S64x64
-    assert sel(0, 0, 3136, 3136, 3136, 1, True, 256) != pg.VARIANT_S64x64_K2
-    # skinny shapes whose long operand is k-contiguous stream
-    assert sel(0, 1, 16384, 64, 4096, 1, True, 256) == pg.VARIANT_T64x64
-    assert sel(0, 0, 16384, 64, 4096, 1, True, 256) == pg.VARIANT_T64x64
+    assert sel(0, 0, 128, 128, 128, 1, True, 256) == pg.VARIANT_S64x64
+    # a skinny dimension with a long operand over 128 MiB streams, whatever
+    # the transposes; one of at most 128 MiB stays with the tiles
+    for tA, tB in ((0, 1), (0, 0), (1, 1), (1, 0)):
+        assert sel(tA, tB, 16384, 64, 4096, 1, True, 256) == pg.VARIANT_T64x64
     assert sel(0, 1, 64, 8192, 8192, 1, True, 256) == pg.VARIANT_T64x64
-    assert sel(1, 1, 16384, 64, 4096, 1, True, 256) != pg.VARIANT_T64x64
+    assert sel(0, 1, 16384, 64, 2048, 1, True, 256) == pg.VARIANT_S64x64_K2
+    assert sel(0, 1, 64, 8192, 4096, 1, True, 256) == pg.VARIANT_S64x64_K2
     assert sel(0, 1, 16384, 64, 128, 1, True, 256) != pg.VARIANT_T64x64
+    # the CU count enters the model: on 64 CUs 2048^3 has four 128 x 128 tiles per CU
+    assert sel(0, 0, 2048, 2048, 2048, 1, True, 64) == pg.VARIANT_M128x128
     # no 4-float loads: the 1-float variant
     assert sel(0, 0, 4092, 4092, 4092, 1, False, 256) == pg.VARIANT_S64x64_V1
     assert sel(3, 0, 4, 4, 4, 1, True, 256) == -1
