@@ -16,7 +16,8 @@
  *   batch item b uses A + b*strideA, B + b*strideB, C + b*strideC.
  *
  * Ownership: A, B and C are DEVICE pointers owned by the caller; the library
- * keeps no reference after the call returns and allocates no memory.
+ * keeps no reference after the call returns and allocates no memory (the
+ * split-K entry points below use a workspace the caller passes in).
  *
  * Execution: every call is asynchronous on `stream` (a hipStream_t; NULL is
  * the default stream) and never synchronises the host. Results are
@@ -46,7 +47,10 @@
  *        where it would be dereferenced. Nothing is launched on error.
  *        The variant-forcing entry points return -18 for an unknown variant
  *        or a 4-float variant the operands cannot use, whatever the
- *        position of their `variant` argument.
+ *        position of their `variant` argument; the split-K entry points
+ *        return -19 for an invalid split count, -20 for an invalid
+ *        workspace and -21 for a workspace too small for a forced split,
+ *        whatever the position of those arguments.
  *    >0  a hipError_t raised when querying the device or launching.
  * sgemm_status_string() turns any status into a message.
  *
@@ -58,6 +62,8 @@
  */
 #ifndef PRECISION_GEMM_AMD_SGEMM_H
 #define PRECISION_GEMM_AMD_SGEMM_H
+
+#include <stddef.h>
 
 #ifdef __cplusplus
 extern "C" {
@@ -164,6 +170,84 @@ int sgemm_batched_variant(int transA, int transB, int M, int N, int K,
                                        const float *const *B_array, int ldb,
                           float beta,        float *const *C_array, int ldc,
                           int batch, int variant, sgemm_stream_t stream);
+
+/*
+ * Split-K forms: the same results as sgemm / sgemm_strided_batched, for grids
+ * whose output tiles are too few to occupy the GPU (a small M x N over a deep
+ * K, e.g. 256 x 256 x 16384, is 16 tiles for 256 compute units). K is cut into
+ * S slices: every (tile, slice) workgroup writes its partial tile to the
+ * workspace, then a second kernel forms
+ *     C = alpha * (partial_0 + partial_1 + ... + partial_{S-1}) + beta * C
+ * summing in slice order, so results are deterministic. This is the split-K
+ * that "From 1% to 94% of cuBLAS, one kernel at a time" finds in cuBLAS when it
+ * compares kernel 10 with cuBLAS at small sizes (a matmul kernel writing
+ * per-slice partial sums, then a reduction kernel adding them).
+ *
+ * workspace: DEVICE memory owned by the caller, 4-byte aligned, of
+ * workspace_bytes bytes; the call uses it until the work completes on
+ * `stream`, so calls that overlap on one workspace race. S slices of every
+ * batch item take S * 4 * M * N * batch bytes. The call picks S itself (the
+ * count that minimises the busiest compute unit's share of the work, with
+ * slices at least 256 deep and at most 128 of them) and takes no more slices
+ * than the workspace holds; with a NULL
+ * workspace, workspace_bytes == 0, or a grid that fills the GPU it runs
+ * exactly like the unsplit form. Whether and how much it splits changes only
+ * the fp32 rounding order, within the accuracy bound above.
+ *
+ * Status codes as above, plus -20 when workspace_bytes > 0 and workspace is
+ * NULL or not 4-byte aligned.
+ */
+int sgemm_ws(int transA, int transB, int M, int N, int K,
+             float alpha, const float *A, int lda,
+                          const float *B, int ldb,
+             float beta,        float *C, int ldc,
+             void *workspace, size_t workspace_bytes,
+             sgemm_stream_t stream);
+
+int sgemm_strided_batched_ws(int transA, int transB, int M, int N, int K,
+                             float alpha, const float *A, int lda,
+                                          const float *B, int ldb,
+                             float beta,        float *C, int ldc,
+                             int batch, long long strideA, long long strideB,
+                             long long strideC,
+                             void *workspace, size_t workspace_bytes,
+                             sgemm_stream_t stream);
+
+/*
+ * Bytes of workspace with which sgemm_strided_batched_ws (or sgemm_ws, with
+ * batch = 1) never takes fewer slices than it would like, on the current
+ * device; 0 when it would not split, for invalid arguments, or when no device
+ * can be queried. The automatic split depends on the device's compute-unit
+ * count, so query on the device that will run the call.
+ */
+size_t sgemm_workspace_size(int transA, int transB, int M, int N, int K, int batch);
+
+/*
+ * sgemm_strided_batched_ws with the variant (as sgemm_strided_batched_variant)
+ * and the split count forced (testing and tuning). splits: 0 = the automatic
+ * choice, 1 = no split, S >= 2 = slices of round_up(ceil(K / S), BK) k each
+ * (BK: the variant's K-step, 16 or 32; the last slice takes the rest, so
+ * fewer than S slices can result). A forced split needs its full workspace
+ * (-21 otherwise) and a tile variant (-19 for SGEMM_VARIANT_T64x64, which
+ * splits K across its own waves instead).
+ */
+int sgemm_strided_batched_ws_variant(int transA, int transB, int M, int N, int K,
+                                     float alpha, const float *A, int lda,
+                                                  const float *B, int ldb,
+                                     float beta,        float *C, int ldc,
+                                     int batch, long long strideA, long long strideB,
+                                     long long strideC, int variant, int splits,
+                                     void *workspace, size_t workspace_bytes,
+                                     sgemm_stream_t stream);
+
+/*
+ * Host-side split decision of the split-K forms for a given variant, exposed
+ * for tests and tuning (no device call): the number of K slices (1 = none)
+ * for this shape on `num_cus` compute units with an unlimited workspace, or a
+ * negative status (-18 for an unknown variant).
+ */
+int sgemm_select_splits(int transA, int transB, int M, int N, int K, int batch,
+                        int variant, int num_cus);
 
 /*
  * Column-major (BLAS convention) forms of sgemm and sgemm_strided_batched:

@@ -17,7 +17,8 @@ import os
 __all__ = [
     "SgemmError", "sgemm", "sgemm_strided_batched", "sgemm_strided_batched_variant",
     "sgemm_batched", "sgemm_batched_variant", "sgemm_colmajor",
-    "sgemm_colmajor_strided_batched", "pointer_array",
+    "sgemm_colmajor_strided_batched", "pointer_array", "sgemm_ws", "sgemm_strided_batched_ws",
+    "sgemm_strided_batched_ws_variant", "sgemm_workspace_size", "sgemm_select_splits",
     "sgemm_status_string", "sgemm_select_variant", "matmul", "library_path",
     "VARIANT_AUTO", "VARIANT_L256x128", "VARIANT_M128x128", "VARIANT_S64x64",
     "VARIANT_S64x64_V1", "VARIANT_T64x64", "VARIANT_L256x256", "VARIANT_S64x64_K2",
@@ -78,6 +79,19 @@ def _load():
     lib.sgemm_batched.argtypes = [i, i, i, i, i, f, p, i, p, i, f, p, i, i, p]
     lib.sgemm_batched_variant.restype = i
     lib.sgemm_batched_variant.argtypes = [i, i, i, i, i, f, p, i, p, i, f, p, i, i, i, p]
+    sz = ctypes.c_size_t
+    lib.sgemm_ws.restype = i
+    lib.sgemm_ws.argtypes = [i, i, i, i, i, f, p, i, p, i, f, p, i, p, sz, p]
+    lib.sgemm_strided_batched_ws.restype = i
+    lib.sgemm_strided_batched_ws.argtypes = [i, i, i, i, i, f, p, i, p, i, f, p, i, i, ll, ll, ll,
+                                             p, sz, p]
+    lib.sgemm_strided_batched_ws_variant.restype = i
+    lib.sgemm_strided_batched_ws_variant.argtypes = [i, i, i, i, i, f, p, i, p, i, f, p, i, i, ll,
+                                                     ll, ll, i, i, p, sz, p]
+    lib.sgemm_workspace_size.restype = sz
+    lib.sgemm_workspace_size.argtypes = [i, i, i, i, i, i]
+    lib.sgemm_select_splits.restype = i
+    lib.sgemm_select_splits.argtypes = [i, i, i, i, i, i, i, i]
     lib.sgemm_colmajor.restype = i
     lib.sgemm_colmajor.argtypes = [i, i, i, i, i, f, p, i, p, i, f, p, i, p]
     lib.sgemm_colmajor_strided_batched.restype = i
@@ -172,6 +186,65 @@ def sgemm_strided_batched_variant(transA, transB, M, N, K, alpha, A, lda, B, ldb
         float(beta), _ptr(C), ldc, batch, strideA, strideB, strideC, int(variant),
         _stream(stream, A, B, C))
     return _check(st, check)
+
+
+def _workspace(ws):
+    """(device address, bytes) of a workspace: a GPU tensor of any dtype (its
+    whole storage), an (address, bytes) pair, or None (no workspace)."""
+    if ws is None:
+        return None, 0
+    if isinstance(ws, tuple):
+        return ws[0], int(ws[1])
+    if hasattr(ws, "data_ptr"):
+        if not ws.is_cuda:
+            raise TypeError("a workspace must be a GPU tensor")
+        return ws.data_ptr(), ws.numel() * ws.element_size()
+    raise TypeError(f"cannot use {type(ws).__name__} as a workspace")
+
+
+def sgemm_ws(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, workspace,
+             stream=None, check=True) -> int:
+    """C ABI ``sgemm_ws`` (split-K with a caller workspace, see _workspace)."""
+    wp, wb = _workspace(workspace)
+    st = _load().sgemm_ws(int(transA), int(transB), M, N, K, float(alpha), _ptr(A), lda,
+                          _ptr(B), ldb, float(beta), _ptr(C), ldc, wp, wb,
+                          _stream(stream, A, B, C))
+    return _check(st, check)
+
+
+def sgemm_strided_batched_ws(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
+                             batch, strideA, strideB, strideC, workspace, stream=None,
+                             check=True) -> int:
+    """C ABI ``sgemm_strided_batched_ws``."""
+    wp, wb = _workspace(workspace)
+    st = _load().sgemm_strided_batched_ws(int(transA), int(transB), M, N, K, float(alpha),
+                                          _ptr(A), lda, _ptr(B), ldb, float(beta), _ptr(C), ldc,
+                                          batch, strideA, strideB, strideC, wp, wb,
+                                          _stream(stream, A, B, C))
+    return _check(st, check)
+
+
+def sgemm_strided_batched_ws_variant(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C,
+                                     ldc, batch, strideA, strideB, strideC, variant, splits,
+                                     workspace, stream=None, check=True) -> int:
+    """C ABI ``sgemm_strided_batched_ws_variant`` (variant and split count forced)."""
+    wp, wb = _workspace(workspace)
+    st = _load().sgemm_strided_batched_ws_variant(
+        int(transA), int(transB), M, N, K, float(alpha), _ptr(A), lda, _ptr(B), ldb,
+        float(beta), _ptr(C), ldc, batch, strideA, strideB, strideC, int(variant), int(splits),
+        wp, wb, _stream(stream, A, B, C))
+    return _check(st, check)
+
+
+def sgemm_workspace_size(transA, transB, M, N, K, batch=1) -> int:
+    """C ABI ``sgemm_workspace_size`` (bytes, for the current device)."""
+    return int(_load().sgemm_workspace_size(int(transA), int(transB), M, N, K, batch))
+
+
+def sgemm_select_splits(transA, transB, M, N, K, batch, variant, num_cus) -> int:
+    """C ABI ``sgemm_select_splits`` (host-side split decision)."""
+    return _load().sgemm_select_splits(int(transA), int(transB), M, N, K, batch, int(variant),
+                                       num_cus)
 
 
 def sgemm_batched(transA, transB, M, N, K, alpha, A_array, lda, B_array, ldb, beta, C_array,

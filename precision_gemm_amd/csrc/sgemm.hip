@@ -76,6 +76,10 @@ struct Params {
     float alpha, beta;
     int tiles_m, tiles_n;
     int group_m;
+    // Split-K (tile kernels only): with splits > 1, flat batch item b is batch
+    // item b / splits and K slice b % splits, covering k in [s*kslice,
+    // min((s+1)*kslice, K)); its partial tile goes to C item b.
+    int splits, kslice;
 };
 
 __device__ __forceinline__ const float *item_a(const Params &p, int b)
@@ -96,8 +100,8 @@ __device__ __forceinline__ float *item_c(const Params &p, int b)
 // pointer-array form, where the host cannot see the item pointers): every
 // thread walks whole dot products over k with 4-byte loads.
 template <int BM, int BN, int NT, bool A_KC, bool B_KC>
-__device__ void plain_tile(const Params &p, const float *Ab, const float *Bb, float *Cb, int m0,
-                           int n0)
+__device__ void plain_tile(const Params &p, const float *Ab, const float *Bb, float *Cb, int K,
+                           int m0, int n0)
 {
     for (int e = threadIdx.x; e < BM * BN; e += NT) {
         const int i = m0 + e / BN, j = n0 + e % BN;
@@ -106,7 +110,7 @@ __device__ void plain_tile(const Params &p, const float *Ab, const float *Bb, fl
         const long long sa_i = A_KC ? (long long)i * p.lda : i, sa_k = A_KC ? 1 : p.lda;
         const long long sb_j = B_KC ? (long long)j * p.ldb : j, sb_k = B_KC ? 1 : p.ldb;
         float acc = 0.0f;
-        for (int k = 0; k < p.K; ++k)
+        for (int k = 0; k < K; ++k)
             acc = __builtin_fmaf(Ab[sa_i + k * sa_k], Bb[sb_j + k * sb_k], acc);
         float *c = Cb + (long long)i * p.ldc + j;
         *c = p.beta == 0.0f ? p.alpha * acc : p.alpha * acc + p.beta * *c;
@@ -332,27 +336,36 @@ sgemm_mfma_kernel(Params p)
     const int wmn = wave % WAVES_MN, kgrp = wave / WAVES_MN;
     const int wm0 = (wmn % WAVES_M) * WM, wn0 = (wmn / WAVES_M) * WN;
 
-    const float *Ab = item_a(p, b), *Bb = item_b(p, b);
+    // This workgroup's K range: the whole K, or its slice under split-K (the
+    // slice's operands start k0 into A and B; kslice is a multiple of BK).
+    int item = b, k0 = 0, Kt = p.K;
+    if (p.splits > 1) {
+        item = b / p.splits;
+        k0 = (b - item * p.splits) * p.kslice;
+        Kt = min(p.kslice, p.K - k0);
+    }
+    const float *Ab = item_a(p, item) + (A_KC ? (long long)k0 : (long long)k0 * p.lda);
+    const float *Bb = item_b(p, item) + (B_KC ? (long long)k0 : (long long)k0 * p.ldb);
     float *Cb = item_c(p, b);
     if (VEC == 4 && (((uintptr_t)Ab | (uintptr_t)Bb) & 15u)) {
-        plain_tile<BM, BN, NT, A_KC, B_KC>(p, Ab, Bb, Cb, m0, n0);
+        plain_tile<BM, BN, NT, A_KC, B_KC>(p, Ab, Bb, Cb, Kt, m0, n0);
         return;
     }
 
     OpA opa;
     opa.X = Ab;
     opa.ld = p.lda;
-    opa.total = A_KC ? (long long)(p.M - 1) * p.lda + p.K : (long long)(p.K - 1) * p.lda + p.M;
+    opa.total = A_KC ? (long long)(p.M - 1) * p.lda + Kt : (long long)(Kt - 1) * p.lda + p.M;
     opa.O = p.M;
-    opa.K = p.K;
+    opa.K = Kt;
     opa.o0 = m0;
     opa.init(tid);
     OpB opb;
     opb.X = Bb;
     opb.ld = p.ldb;
-    opb.total = B_KC ? (long long)(p.N - 1) * p.ldb + p.K : (long long)(p.K - 1) * p.ldb + p.N;
+    opb.total = B_KC ? (long long)(p.N - 1) * p.ldb + Kt : (long long)(Kt - 1) * p.ldb + p.N;
     opb.O = p.N;
-    opb.K = p.K;
+    opb.K = Kt;
     opb.o0 = n0;
     opb.init(tid);
 
@@ -364,7 +377,7 @@ sgemm_mfma_kernel(Params p)
             acc[i][j] = f32x16{};
 
     f32x4 ra[OpA::SLOTS], rb[OpB::SLOTS];
-    const int nsteps = (p.K + BK - 1) / BK;
+    const int nsteps = (Kt + BK - 1) / BK;
 
     // EVEN_K: every K-step is full and no load carries a k mask. Otherwise
     // only the copies of the loop body that can load the partial last step
@@ -561,7 +574,7 @@ sgemm_mfma_kernel(Params p)
 
 // ---------------------------------------------------------------------------
 // Streaming kernel for few, deep tiles (a skinny N, or a grid too small to give
-// every CU a large tile): a 64 x 64 tile per workgroup whose four waves each
+// every CU a large tile; never launched with split-K): a 64 x 64 tile per workgroup whose four waves each
 // own every fourth K-step (wave w takes steps w, w+4, ...) and accumulate the
 // whole tile over their steps. Every wave fills its own ring of STAGES LDS
 // buffers with direct-to-LDS 16-byte buffer loads (buffer_load_dwordx4 ... lds:
@@ -726,7 +739,7 @@ sgemm_stream_kernel(Params p)
     const float *Ab = item_a(p, b), *Bb = item_b(p, b);
     float *Cb = item_c(p, b);
     if (((uintptr_t)Ab | (uintptr_t)Bb) & 15u) {
-        plain_tile<BM, BN, 64 * WAVES, A_KC, B_KC>(p, Ab, Bb, Cb, m0, n0);
+        plain_tile<BM, BN, 64 * WAVES, A_KC, B_KC>(p, Ab, Bb, Cb, p.K, m0, n0);
         return;
     }
 
@@ -892,6 +905,31 @@ __global__ void __launch_bounds__(256) sgemm_scale_kernel(float *C, float *const
     }
 }
 
+// Split-K epilogue: C = alpha * (sum of the item's partial tiles, slice 0
+// first) + beta * C over the M x N window of every batch item. W holds the
+// partials of item i, slice s at W + (i * splits + s) * M * N, rows of N.
+// The summation order is fixed, so results do not depend on timing.
+__global__ void __launch_bounds__(256) sgemm_splitk_reduce_kernel(const float *W, float *C,
+                                                                  float *const *Carr, int M,
+                                                                  int N, int ldc, long long sC,
+                                                                  int items, int splits,
+                                                                  float alpha, float beta)
+{
+    const long long per = (long long)M * N;
+    const long long total = per * items;
+    for (long long e = blockIdx.x * 256LL + threadIdx.x; e < total;
+         e += (long long)gridDim.x * 256) {
+        const long long item = e / per, in_item = e - item * per;
+        const long long r = in_item / N, c = in_item - r * N;
+        const float *w = W + item * splits * per + in_item;
+        float sum = w[0];
+        for (int sl = 1; sl < splits; ++sl)
+            sum += w[sl * per];
+        float *x = (Carr ? Carr[item] : C + item * sC) + r * ldc + c;
+        *x = beta == 0.0f ? alpha * sum : alpha * sum + beta * *x;
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Host side
 // ---------------------------------------------------------------------------
@@ -1051,6 +1089,62 @@ extern "C" int sgemm_select_variant(int transA, int transB, int M, int N, int K,
 
 namespace {
 
+constexpr int kMinSliceK = 256; // shortest K slice worth a workgroup of its own
+constexpr int kSliceCostK = 256; // a workgroup's fixed cost (pipeline fill, epilogue) in k
+constexpr int kMaxSplits = 128;
+
+// Split count for `variant` (a tile kernel): the S that minimises the busiest
+// CU's work, ceil(tiles * S / CUs) workgroups of (K / S + kSliceCostK) k each,
+// over slices at least kMinSliceK deep and at most kMaxSplits of them. A
+// slice is round_up(ceil(K / S), BK) long, so the returned count is that of
+// the non-empty slices; 1 means no split.
+long long splits_for(int variant, int M, int N, int K, int batch, long long cus, int *kslice)
+{
+    const VariantInfo &vi = kVariants[variant];
+    *kslice = K;
+    if (M == 0 || N == 0 || K == 0 || batch == 0)
+        return 1;
+    const long long tiles = ceil_div(M, vi.bm) * ceil_div(N, vi.bn) * batch;
+    long long smax = K / kMinSliceK;
+    if (smax > kMaxSplits)
+        smax = kMaxSplits;
+    long long best_s = 1, best_ks = K;
+    long long best_cost = ceil_div(tiles, cus) * ((long long)K + kSliceCostK);
+    for (long long S = 2; S <= smax; ++S) {
+        const long long ks = ceil_div(ceil_div(K, S), vi.bk) * vi.bk;
+        const long long se = ceil_div(K, ks);
+        const long long cost = ceil_div(tiles * se, cus) * (ks + kSliceCostK);
+        if (cost < best_cost) {
+            best_cost = cost;
+            best_s = se;
+            best_ks = ks;
+        }
+    }
+    *kslice = (int)best_ks;
+    return best_s;
+}
+
+} // namespace
+
+extern "C" int sgemm_select_splits(int transA, int transB, int M, int N, int K, int batch,
+                                   int variant, int num_cus)
+{
+    if (transA != 0 && transA != 1) return -1;
+    if (transB != 0 && transB != 1) return -2;
+    if (M < 0) return -3;
+    if (N < 0) return -4;
+    if (K < 0) return -5;
+    if (batch < 0) return -14;
+    if (variant < 0 || variant >= SGEMM_VARIANT_COUNT)
+        return -18;
+    if (variant == SGEMM_VARIANT_T64x64)
+        return 1;
+    int kslice = 0;
+    return (int)splits_for(variant, M, N, K, batch, num_cus < 1 ? 1 : num_cus, &kslice);
+}
+
+namespace {
+
 // One validated call in row-major terms. Either the strided bases (A, B, C
 // with sA, sB, sC) or the pointer arrays (Aarr, Barr, Carr) describe the
 // batch items.
@@ -1066,7 +1160,15 @@ struct Call {
     float *const *Carr;
 };
 
-int launch(const Call &c, int variant, hipStream_t s)
+// Workspace of a split-K call: `ws` (4-byte aligned, or NULL) of `ws_bytes`.
+// splits: 0 = choose (only with a workspace), 1 = none, >= 2 forced.
+struct Split {
+    float *ws;
+    size_t ws_bytes;
+    int splits;
+};
+
+int launch(const Call &c, int variant, hipStream_t s, Split sk = Split{nullptr, 0, 1})
 {
     if (c.M == 0 || c.N == 0 || c.batch == 0)
         return 0;
@@ -1094,16 +1196,67 @@ int launch(const Call &c, int variant, hipStream_t s)
         (arrays || (aligned16(c.A) && aligned16(c.B) && c.sA % 4 == 0 && c.sB % 4 == 0)) &&
         c.lda % 4 == 0 && c.ldb % 4 == 0 && (a_kc ? c.K % 4 == 0 : c.M % 4 == 0) &&
         (b_kc ? c.K % 4 == 0 : c.N % 4 == 0);
-    if (variant == SGEMM_VARIANT_AUTO) {
-        int cus = 0;
+    const bool auto_variant = variant == SGEMM_VARIANT_AUTO;
+    int cus = 0;
+    if (auto_variant || sk.splits == 0) {
         const int st = num_cus_of_current_device(&cus);
         if (st != 0)
             return st;
+    }
+    if (auto_variant) {
         variant = sgemm_select_variant(c.tA, c.tB, c.M, c.N, c.K, c.batch, vec4_ok ? 1 : 0, cus);
         if (variant < 0)
             return variant;
     } else if (kVariants[variant].vec == 4 && !vec4_ok) {
         return -18;
+    }
+
+    // Split-K: the tile kernels write per-slice partial tiles into the
+    // workspace and a second kernel sums them in slice order.
+    const long long part_bytes = 4LL * c.M * c.N * c.batch; // one slice of every item
+    int splits = 1, kslice = c.K;
+    if (sk.splits == 0 && sk.ws != nullptr) {
+        int v = variant;
+        long long S = v == SGEMM_VARIANT_T64x64 ? 1 : splits_for(v, c.M, c.N, c.K, c.batch, cus, &kslice);
+        if (auto_variant && v == SGEMM_VARIANT_T64x64) {
+            // A grid too small even for the streaming kernel's CUs: split the
+            // 64 x 64 tile across workgroups instead.
+            const int alt = c.K >= 768 ? SGEMM_VARIANT_S64x64_K2 : SGEMM_VARIANT_S64x64;
+            const long long S2 = splits_for(alt, c.M, c.N, c.K, c.batch, cus, &kslice);
+            if (S2 >= 2) {
+                v = alt;
+                S = S2;
+            }
+        }
+        const long long fit = (long long)(sk.ws_bytes / (size_t)part_bytes);
+        if (S > fit) {
+            // Fewer slices, as many as the workspace holds.
+            S = fit;
+            if (S >= 2) {
+                const int bk = kVariants[v].bk;
+                const long long ks = ceil_div(ceil_div(c.K, S), bk) * bk;
+                kslice = (int)ks;
+                S = ceil_div(c.K, ks);
+            }
+        }
+        if (S >= 2) {
+            variant = v;
+            splits = (int)S;
+        } else {
+            kslice = c.K;
+        }
+    } else if (sk.splits >= 2) {
+        if (variant == SGEMM_VARIANT_T64x64)
+            return -19;
+        const int bk = kVariants[variant].bk;
+        const long long ks = ceil_div(ceil_div(c.K, sk.splits), bk) * bk;
+        const long long S = ceil_div(c.K, ks);
+        if (S >= 2) {
+            if ((size_t)(S * part_bytes) > sk.ws_bytes)
+                return -21;
+            splits = (int)S;
+            kslice = (int)ks;
+        }
     }
 
     const VariantInfo &vi = kVariants[variant];
@@ -1129,31 +1282,61 @@ int launch(const Call &c, int variant, hipStream_t s)
     p.tiles_m = (int)ceil_div(c.M, vi.bm);
     p.tiles_n = (int)ceil_div(c.N, vi.bn);
     p.group_m = 8;
+    p.splits = splits;
+    p.kslice = kslice;
+    if (splits > 1) {
+        // Partial tiles: C item (batch item, slice) is a dense M x N block of
+        // the workspace, written plainly (alpha 1, beta 0).
+        p.C = sk.ws;
+        p.Carr = nullptr;
+        p.ldc = c.N;
+        p.sC = (long long)c.M * c.N;
+        p.alpha = 1.0f;
+        p.beta = 0.0f;
+    }
     const long long per_batch = (long long)p.tiles_m * p.tiles_n;
-    // Keep one launch's workgroup count within 2^31 and its batch axis within 65535.
-    long long max_items = ((1LL << 31) - 1) / per_batch;
-    if (max_items > 65535)
-        max_items = 65535;
-    if (max_items < 1)
+    const long long flat = (long long)c.batch * splits; // workgroup rows: (item, slice)
+    // Keep one launch's workgroup count within 2^31 and its batch axis within
+    // 65535, in whole items.
+    long long max_flat = ((1LL << 31) - 1) / per_batch;
+    if (max_flat > 65535)
+        max_flat = 65535;
+    max_flat -= max_flat % splits;
+    if (max_flat < 1)
         return -3;
     KernelFn fn = vi.fn[c.tA][c.tB][even_k];
-    for (long long b0 = 0; b0 < c.batch; b0 += max_items) {
-        const long long nb = c.batch - b0 < max_items ? c.batch - b0 : max_items;
+    for (long long b0 = 0; b0 < flat; b0 += max_flat) {
+        const long long nb = flat - b0 < max_flat ? flat - b0 : max_flat;
+        const long long i0 = b0 / splits; // first batch item of this launch
         Params q = p;
         if (arrays) {
-            q.Aarr = c.Aarr + b0;
-            q.Barr = c.Barr + b0;
-            q.Carr = c.Carr + b0;
+            q.Aarr = c.Aarr + i0;
+            q.Barr = c.Barr + i0;
+            if (splits == 1)
+                q.Carr = c.Carr + i0;
         } else {
-            q.A = c.A + b0 * c.sA;
-            q.B = c.B + b0 * c.sB;
-            q.C = c.C + b0 * c.sC;
+            q.A = c.A + i0 * c.sA;
+            q.B = c.B + i0 * c.sB;
         }
+        q.C = splits > 1 ? p.C + b0 * p.sC : (arrays ? nullptr : c.C + i0 * c.sC);
         void *args[] = {&q};
         hipError_t e = hipLaunchKernel((const void *)fn, dim3((unsigned)per_batch, (unsigned)nb),
                                        dim3(vi.threads), args, 0, s);
         if (e != hipSuccess)
             return (int)e;
+    }
+    if (splits > 1) {
+        const long long total = (long long)c.M * c.N * c.batch;
+        const long long blocks = ceil_div(total, 256) < 8192 ? ceil_div(total, 256) : 8192;
+        const float *W = sk.ws;
+        float *C = c.C;
+        float *const *Carr = c.Carr;
+        int M = c.M, N = c.N, ldc = c.ldc, items = c.batch;
+        long long sC = c.sC;
+        float alpha = c.alpha, beta = c.beta;
+        void *args[] = {&W, &C, &Carr, &M, &N, &ldc, &sC, &items, &splits, &alpha, &beta};
+        return (int)hipLaunchKernel((const void *)sgemm_splitk_reduce_kernel, dim3((unsigned)blocks),
+                                    dim3(256), args, 0, s);
     }
     return 0;
 }
@@ -1205,6 +1388,74 @@ extern "C" int sgemm_strided_batched_variant(int transA, int transB, int M, int 
     const Call c{transA, transB, M, N, K, alpha, beta, A, B, C, lda, ldb, ldc, batch,
                  strideA, strideB, strideC, nullptr, nullptr, nullptr};
     return launch(c, variant, reinterpret_cast<hipStream_t>(stream));
+}
+
+extern "C" int sgemm_strided_batched_ws_variant(int transA, int transB, int M, int N, int K,
+                                                float alpha, const float *A, int lda,
+                                                const float *B, int ldb, float beta, float *C,
+                                                int ldc, int batch, long long strideA,
+                                                long long strideB, long long strideC, int variant,
+                                                int splits, void *workspace,
+                                                size_t workspace_bytes, sgemm_stream_t stream)
+{
+    const int st = validate(transA, transB, M, N, K, A, lda, B, ldb, C, ldc, batch, strideA,
+                            strideB, strideC, alpha, beta);
+    if (st != 0)
+        return st;
+    if (variant < SGEMM_VARIANT_AUTO || variant >= SGEMM_VARIANT_COUNT)
+        return -18;
+    if (splits < 0 || splits > 65535)
+        return -19;
+    if (workspace_bytes > 0 && (workspace == nullptr || ((uintptr_t)workspace & 3u)))
+        return -20;
+    const Call c{transA, transB, M, N, K, alpha, beta, A, B, C, lda, ldb, ldc, batch,
+                 strideA, strideB, strideC, nullptr, nullptr, nullptr};
+    const Split sk{workspace_bytes > 0 ? static_cast<float *>(workspace) : nullptr,
+                   workspace_bytes, splits};
+    return launch(c, variant, reinterpret_cast<hipStream_t>(stream), sk);
+}
+
+extern "C" int sgemm_strided_batched_ws(int transA, int transB, int M, int N, int K, float alpha,
+                                        const float *A, int lda, const float *B, int ldb,
+                                        float beta, float *C, int ldc, int batch,
+                                        long long strideA, long long strideB, long long strideC,
+                                        void *workspace, size_t workspace_bytes,
+                                        sgemm_stream_t stream)
+{
+    return sgemm_strided_batched_ws_variant(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta,
+                                            C, ldc, batch, strideA, strideB, strideC,
+                                            SGEMM_VARIANT_AUTO, 0, workspace, workspace_bytes,
+                                            stream);
+}
+
+extern "C" int sgemm_ws(int transA, int transB, int M, int N, int K, float alpha, const float *A,
+                        int lda, const float *B, int ldb, float beta, float *C, int ldc,
+                        void *workspace, size_t workspace_bytes, sgemm_stream_t stream)
+{
+    return sgemm_strided_batched_ws(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
+                                    1, 0, 0, 0, workspace, workspace_bytes, stream);
+}
+
+extern "C" size_t sgemm_workspace_size(int transA, int transB, int M, int N, int K, int batch)
+{
+    if ((transA != 0 && transA != 1) || (transB != 0 && transB != 1) || M <= 0 || N <= 0 ||
+        K <= 0 || batch <= 0)
+        return 0;
+    int cus = 0;
+    if (num_cus_of_current_device(&cus) != 0)
+        return 0;
+    // The largest split the automatic path makes: it assumes 4-float loads
+    // (larger tiles, so no more slices than the 1-float path) and also the
+    // 64 x 64 tile that replaces the streaming kernel on tiny grids.
+    const int v = sgemm_select_variant(transA, transB, M, N, K, batch, 1, cus);
+    int kslice = 0;
+    long long S = v == SGEMM_VARIANT_T64x64 ? 1 : splits_for(v, M, N, K, batch, cus, &kslice);
+    const long long S2 = splits_for(SGEMM_VARIANT_S64x64, M, N, K, batch, cus, &kslice);
+    if (v == SGEMM_VARIANT_T64x64 && S2 > S)
+        S = S2;
+    if (S < 2)
+        return 0;
+    return (size_t)(S * 4LL * M * N * batch);
 }
 
 extern "C" int sgemm_strided_batched(int transA, int transB, int M, int N, int K, float alpha,
@@ -1307,6 +1558,9 @@ extern "C" const char *sgemm_status_string(int status)
     case -16: return "invalid argument 16 (strideB < 0)";
     case -17: return "invalid argument 17 (strideC < 0)";
     case -18: return "invalid variant argument (unknown variant, or a 4-float variant for unaligned operands)";
+    case -19: return "invalid split count (negative, over 65535, or a split of the streaming variant)";
+    case -20: return "invalid workspace (NULL or not 4-byte aligned while workspace_bytes > 0)";
+    case -21: return "workspace too small for the requested split count";
     default: break;
     }
     if (status < 0)

@@ -153,3 +153,70 @@ def test_select_variant(pg):
     # no 4-float loads: the 1-float variant
     assert sel(0, 0, 4092, 4092, 4092, 1, False, 256) == pg.VARIANT_S64x64_V1
     assert sel(3, 0, 4, 4, 4, 1, True, 256) == -1
+
+
+# ------------------------------------------------------------------ split-K (host side)
+
+def test_select_splits(pg):
+    sel = pg.sgemm_select_splits
+    K2, S64, M128, T = (pg.VARIANT_S64x64_K2, pg.VARIANT_S64x64, pg.VARIANT_M128x128,
+                        pg.VARIANT_T64x64)
+    # 16 tiles of 64 x 64 on 256 CUs: 16 slices of 1024, one workgroup per CU
+    assert sel(0, 0, 256, 256, 16384, 1, K2, 256) == 16
+    assert sel(0, 0, 256, 256, 16384, 1, K2, 64) == 4
+    # a full grid does not split
+    assert sel(0, 0, 1024, 1024, 1024, 1, K2, 256) == 1
+    assert sel(0, 0, 1024, 1024, 4096, 1, K2, 256) == 1
+    assert sel(0, 0, 1024, 1024, 8192, 1, M128, 256) == 4       # 64 tiles of 128 x 128
+    # 144 tiles: two slices would leave some CUs two workgroups of half the
+    # work (no gain); seven put at most four short ones on a CU
+    assert sel(0, 0, 768, 768, 16384, 1, K2, 256) == 7
+    # at most 128 slices
+    assert sel(0, 1, 64, 64, 1 << 18, 1, K2, 256) == 128
+    # slices are at least 256 deep
+    assert sel(0, 0, 128, 128, 128, 1, S64, 256) == 1
+    assert sel(0, 0, 128, 128, 4096, 1, S64, 256) == 16
+    # the slice length is rounded up to the K-step, so the count can drop:
+    # 1000 / 3 -> 336 (BK 16) -> 3 slices; 1000 / 3 -> 352 (BK 32) -> 3 slices
+    assert sel(0, 0, 64, 64, 1000, 1, S64, 256) == 3
+    assert sel(0, 0, 64, 64, 1000, 1, K2, 256) == 3
+    assert sel(0, 0, 64, 64, 600, 1, K2, 256) == 2
+    # batch items count as tiles
+    assert sel(0, 0, 64, 64, 8192, 64, K2, 256) == 4
+    # the streaming kernel splits K across its own waves
+    assert sel(0, 1, 64, 64, 1 << 20, 1, T, 256) == 1
+    assert sel(0, 0, 64, 64, 4096, 1, pg.VARIANT_COUNT, 256) == -18
+    assert sel(0, 0, -1, 64, 4096, 1, K2, 256) == -3
+
+
+def ws_call(pg, variant=-1, splits=0, ws=None, **over):
+    a = base_args(**over)
+    return pg.sgemm_strided_batched_ws_variant(
+        a["transA"], a["transB"], a["M"], a["N"], a["K"], a["alpha"], a["A"], a["lda"],
+        a["B"], a["ldb"], a["beta"], a["C"], a["ldc"], a["batch"], a["strideA"], a["strideB"],
+        a["strideC"], variant, splits, ws, check=False)
+
+
+def test_split_arguments_checked(pg):
+    # the ordinary argument checks come first
+    assert ws_call(pg, M=-1) == -3
+    assert ws_call(pg, splits=-1) == -19
+    assert ws_call(pg, splits=1 << 16) == -19
+    assert ws_call(pg, ws=(0, 64)) == -20                 # NULL with a size
+    assert ws_call(pg, ws=(FAKE + 2, 64)) == -20          # not 4-byte aligned
+    assert ws_call(pg, variant=pg.VARIANT_COUNT) == -18
+    # a forced split needs its whole workspace: 4 slices of 64 x 64 = 64 KiB
+    # (checked before any device work, as the variant is forced too)
+    kw = dict(M=64, N=64, K=4096, lda=4096, ldb=64, ldc=64)
+    assert ws_call(pg, variant=pg.VARIANT_S64x64, splits=4, ws=(FAKE, 4 * 64 * 64 * 4 - 4),
+                   **kw) == -21
+    assert ws_call(pg, variant=pg.VARIANT_T64x64, splits=4, ws=(FAKE, 1 << 20), **kw) == -19
+    for st in (-19, -20, -21):
+        assert "invalid" in pg.sgemm_status_string(st) or "too small" in \
+            pg.sgemm_status_string(st)
+
+
+def test_workspace_size_without_a_device(pg):
+    # no device to query here: the size is 0 (and invalid shapes are always 0)
+    assert pg.sgemm_workspace_size(0, 0, 256, 256, 16384, 1) >= 0
+    assert pg.sgemm_workspace_size(0, 0, -1, 256, 16384, 1) == 0

@@ -595,3 +595,132 @@ def test_colmajor_against_definition(env, tA, tB):
                     rep = oracle.bound_check(got, ref, S, Cm[b], alpha, beta, K)
                     assert rep.ok, (form, b, rep)
             assert np.array_equal(out[~written].view(np.uint32), hC[~written].view(np.uint32))
+
+
+# ------------------------------------------------------------------ split-K
+
+def run_gpu_ws(env, w: Workload, A, B, C, variant=-1, splits=0, ws_floats=None):
+    """As run_gpu, through sgemm_strided_batched_ws_variant with a workspace of
+    ws_floats floats (None: what sgemm_workspace_size asks for, at least one
+    float). The workspace carries guard bands too."""
+    torch, pg = env
+    dev = torch.device("cuda:0")
+    if ws_floats is None:
+        ws_floats = max(1, pg.sgemm_workspace_size(w.trans_a, w.trans_b, w.M, w.N, w.K,
+                                                   w.batch) // 4)
+
+    def put(x):
+        buf = torch.full((x.size + 2 * GUARD,), -7.25, dtype=torch.float32, device=dev)
+        buf[GUARD:GUARD + x.size] = torch.from_numpy(x).to(dev)
+        return buf
+
+    dA, dB, dC = put(A), put(B), put(C)
+    ws = torch.full((ws_floats + 2 * GUARD,), 3.5, dtype=torch.float32, device=dev)
+    st = pg.sgemm_strided_batched_ws_variant(
+        w.trans_a, w.trans_b, w.M, w.N, w.K, w.alpha, dA.data_ptr() + 4 * GUARD, w.LDA,
+        dB.data_ptr() + 4 * GUARD, w.LDB, w.beta, dC.data_ptr() + 4 * GUARD, w.LDC, w.batch,
+        w.SA, w.SB, w.SC, variant, splits, (ws.data_ptr() + 4 * GUARD, 4 * ws_floats),
+        stream=torch.cuda.current_stream(dev).cuda_stream, check=False)
+    torch.cuda.synchronize(dev)
+    whole, wsh = dC.cpu().numpy(), ws.cpu().numpy()
+    assert np.all(whole[:GUARD] == np.float32(-7.25)) and \
+        np.all(whole[GUARD + C.size:] == np.float32(-7.25)), "a guard band around C was overwritten"
+    assert np.all(wsh[:GUARD] == np.float32(3.5)) and \
+        np.all(wsh[GUARD + ws_floats:] == np.float32(3.5)), "a write past the workspace"
+    return st, whole[GUARD:GUARD + C.size]
+
+
+SPLIT_VARIANTS = [v for v in ALL_VARIANTS if v != 4]  # every tile kernel (not the streaming one)
+
+
+@pytest.mark.parametrize("variant", SPLIT_VARIANTS)
+def test_splitk_bitwise(env, variant):
+    """Forced split counts on every tile variant and transpose pair, ragged
+    M/N, K not a multiple of the slice, batches with gaps, integer inputs:
+    bitwise equal to the oracle, nothing written outside C's windows or the
+    workspace."""
+    _, pg = env
+    n_run = 0
+    for (M, N, K, batch), (tA, tB) in itertools.product(
+            [(68, 132, 1000, 1), (36, 20, 2048, 3), (260, 64, 776, 2)],
+            itertools.product([0, 1], repeat=2)):
+        for splits in (2, 3, 7):
+            alpha, beta = (2.0, -1.0) if splits != 3 else (0.5, 0.0)
+            w = Workload(f"sk{M}x{N}x{K}", tA, tB, M, N, K, alpha, beta, seed=M + K + splits,
+                         dist="int3", batch=batch, lda=(M if tA else K) + 4,
+                         ldb=(K if tB else N) + 8, ldc=N + 4)
+            w = Workload(**{**w.__dict__, "stride_a": w.SA + 8, "stride_b": w.SB + 4,
+                            "stride_c": w.SC + 12})
+            A, B, C = workloads.make_inputs(w)
+            log(f"[split-K] variant {variant} {M}x{N}x{K} b{batch} tA={tA} tB={tB} S={splits}")
+            st, got = run_gpu_ws(env, w, A, B, C, variant=variant, splits=splits,
+                                 ws_floats=splits * M * N * batch)
+            assert st == 0, (w, st)
+            check_against_oracle(w, A, B, C, got, exact=True)
+            check_untouched(w, C, got)
+            n_run += 1
+    assert n_run == 36
+
+
+def test_splitk_automatic(env):
+    """The automatic split: deep-K shapes with few tiles split (fp32 within
+    the bound; the workspace size query is large enough); a workspace of a
+    third of that still gives correct results with fewer slices; no
+    workspace, or a grid that fills the GPU, gives the unsplit call's bits."""
+    torch, pg = env
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    for tA, tB, M, N, K, batch in ((0, 0, 256, 256, 16384, 1), (1, 1, 100, 72, 9000, 2),
+                                   (0, 1, 64, 64, 4096, 1), (1, 0, 128, 200, 3000, 1)):
+        w = Workload(f"auto{M}x{N}x{K}", tA, tB, M, N, K, 0.75, 1.5, seed=K, dist="normal",
+                     batch=batch)
+        A, B, C = workloads.make_inputs(w)
+        need = pg.sgemm_workspace_size(tA, tB, M, N, K, batch)
+        assert need >= 2 * 4 * M * N * batch, (w, need, cus)
+        log(f"[split-K auto] {M}x{N}x{K} b{batch} tA={tA} tB={tB} workspace {need} B")
+        for ws_floats in (need // 4, need // 12):
+            st, got = run_gpu_ws(env, w, A, B, C, ws_floats=ws_floats)
+            assert st == 0
+            check_against_oracle(w, A, B, C, got)
+            check_untouched(w, C, got)
+        # no workspace: exactly the unsplit call
+        st, got = run_gpu_ws(env, w, A, B, C, ws_floats=0)
+        st2, ref = run_gpu(env, w, A, B, C)
+        assert st == st2 == 0
+        assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+    # a full grid does not split: the same bits as the plain call
+    w = Workload("full", 0, 0, 1024, 1024, 1024, 1.0, 0.5, seed=3)
+    A, B, C = workloads.make_inputs(w)
+    assert pg.sgemm_workspace_size(0, 0, 1024, 1024, 1024, 1) == 0
+    st, got = run_gpu_ws(env, w, A, B, C, ws_floats=1 << 20)
+    st2, ref = run_gpu(env, w, A, B, C)
+    assert st == st2 == 0
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+
+
+def test_splitk_deterministic(env):
+    """Two launches of the same split call give the same bits, and the
+    single-matrix entry point sgemm_ws matches the strided form."""
+    torch, pg = env
+    dev = torch.device("cuda:0")
+    M, N, K = 192, 160, 12000
+    g = torch.Generator(device=dev).manual_seed(5)
+    A = torch.randn(M, K, device=dev, generator=g)
+    B = torch.randn(K, N, device=dev, generator=g)
+    ws = torch.empty(pg.sgemm_workspace_size(0, 0, M, N, K) // 4 + 1, device=dev)
+    outs = []
+    for form in ("ws", "ws", "strided"):
+        C = torch.zeros(M, N, device=dev)
+        if form == "ws":
+            pg.sgemm_ws(0, 0, M, N, K, 1.0, A, K, B, N, 0.0, C, N, ws)
+        else:
+            pg.sgemm_strided_batched_ws(0, 0, M, N, K, 1.0, A, K, B, N, 0.0, C, N, 1, 0, 0, 0,
+                                        ws)
+        torch.cuda.synchronize(dev)
+        outs.append(C.cpu().numpy())
+    assert np.array_equal(outs[0].view(np.uint32), outs[1].view(np.uint32))
+    assert np.array_equal(outs[0].view(np.uint32), outs[2].view(np.uint32))
+    ref, S = oracle.sgemm_rows(0, 0, M, N, K, 1.0, A.cpu().numpy().reshape(-1), K,
+                               B.cpu().numpy().reshape(-1), N, 0.0,
+                               np.zeros(M * N, np.float32), N)
+    rep = oracle.bound_check(outs[0], ref[0], S[0], np.zeros((M, N), np.float32), 1.0, 0.0, K)
+    assert rep.ok, rep
