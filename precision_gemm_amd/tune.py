@@ -2,6 +2,7 @@
 far the library's automatic choice is from the fastest one.
 
     python -m precision_gemm_amd.tune [--shapes default|quick] [--json out.json]
+    python -m precision_gemm_amd.tune --splitk [--json out.json]
 
 For each shape every applicable variant is timed on the same device buffers,
 interleaved over several rounds (so clock drift hits all variants alike); a
@@ -138,12 +139,95 @@ def sweep(shapes, rounds: int = 3, target_ms: float = 20.0, out=sys.stdout):
     return results
 
 
+# Deep-K shapes with few output tiles, for the split-K comparison.
+SPLITK_SHAPES = [
+    (0, 0, 256, 256, 4096, 1), (0, 0, 256, 256, 16384, 1), (0, 0, 128, 128, 65536, 1),
+    (0, 0, 512, 512, 8192, 1), (1, 0, 512, 512, 16384, 1), (0, 0, 640, 640, 8192, 1),
+    (0, 0, 768, 768, 16384, 1), (0, 1, 64, 64, 262144, 1), (0, 0, 64, 64, 8192, 16),
+    (0, 0, 1024, 1024, 4096, 1), (0, 0, 1024, 1024, 16384, 1),
+]
+
+
+def splitk_sweep(shapes, rounds: int = 3, target_ms: float = 20.0, out=sys.stdout):
+    """Time the plain automatic call against the split-K automatic call (with
+    the workspace sgemm_workspace_size asks for) on each shape."""
+    import torch
+
+    import precision_gemm_amd as pg
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    gen = torch.Generator(device=dev).manual_seed(1234)
+    X = torch.rand(4096, 4096, device=dev, generator=gen)
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < 0.4:
+        pg.sgemm(0, 0, 4096, 4096, 4096, 1.0, X, 4096, X, 4096, 0.0, X, 4096)
+        torch.cuda.synchronize(dev)
+    del X
+    results = []
+    for tA, tB, M, N, K, batch in shapes:
+        def buf(rows, cols):
+            return torch.rand((batch, rows, cols), device=dev, generator=gen) * 2 - 1
+        A = buf(K, M) if tA else buf(M, K)
+        B = buf(N, K) if tB else buf(K, N)
+        C = buf(M, N)
+        lda, ldb = A.shape[2], B.shape[2]
+        sa, sb, sc = A.stride(0), B.stride(0), C.stride(0)
+        need = pg.sgemm_workspace_size(tA, tB, M, N, K, batch)
+        ws = torch.empty(max(1, need // 4), device=dev)
+        v = pg.sgemm_select_variant(tA, tB, M, N, K, batch, 1, cus)
+        vs = pg.VARIANT_S64x64_K2 if v == pg.VARIANT_T64x64 else v
+        splits = pg.sgemm_select_splits(tA, tB, M, N, K, batch, vs, cus) if need else 1
+        calls = {
+            "plain": lambda: pg.sgemm_strided_batched(tA, tB, M, N, K, 1.0, A, lda, B, ldb, 0.0,
+                                                      C, N, batch, sa, sb, sc,
+                                                      stream=stream.cuda_stream),
+            "split": lambda: pg.sgemm_strided_batched_ws(tA, tB, M, N, K, 1.0, A, lda, B, ldb,
+                                                         0.0, C, N, batch, sa, sb, sc, ws,
+                                                         stream=stream.cuda_stream),
+        }
+        launches = {}
+        for k, call in calls.items():
+            call()
+            torch.cuda.synchronize(dev)
+            one = time_variant(torch, pg, stream, call, 3)
+            launches[k] = max(3, min(500, int(target_ms * 1e3 / max(one, 1.0))))
+        times = {k: [] for k in calls}
+        for _ in range(rounds):
+            for k in calls:
+                time_variant(torch, pg, stream, calls[k], max(2, launches[k] // 2))
+                times[k].append(time_variant(torch, pg, stream, calls[k], launches[k]))
+        med = {k: statistics.median(t) for k, t in times.items()}
+        flops = 2.0 * M * N * K * batch
+        row = {"shape": {"transA": tA, "transB": tB, "M": M, "N": N, "K": K, "batch": batch},
+               "variant": pg.VARIANT_NAMES[vs if need else v], "splits": splits,
+               "workspace_bytes": need, "plain_us": round(med["plain"], 2),
+               "split_us": round(med["split"], 2),
+               "split_tflops": round(flops / med["split"] / 1e6, 1),
+               "speedup": round(med["plain"] / med["split"], 2)}
+        results.append(row)
+        print(f"{'NT'[tA]}{'NT'[tB]} {M}x{N}x{K} b{batch}: plain {med['plain']:.1f} us, split-K "
+              f"S={splits} ({row['variant']}, workspace {need} B) {med['split']:.1f} us "
+              f"({row['split_tflops']} TFLOP/s), x{row['speedup']}", file=out, flush=True)
+        del A, B, C, ws
+    return results
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--shapes", choices=["default", "quick"], default="default")
+    ap.add_argument("--splitk", action="store_true",
+                    help="compare the plain and split-K automatic calls on deep-K shapes")
     ap.add_argument("--rounds", type=int, default=3)
     ap.add_argument("--json", default=None, help="write the table as JSON here")
     args = ap.parse_args(argv)
+    if args.splitk:
+        res = splitk_sweep(SPLITK_SHAPES, rounds=args.rounds)
+        if args.json:
+            with open(args.json, "w") as f:
+                json.dump(res, f, indent=1)
+        return 0
     shapes = DEFAULT_SHAPES if args.shapes == "default" else QUICK_SHAPES
     res = sweep(shapes, rounds=args.rounds)
     regrets = [r["regret"] for r in res]
