@@ -724,3 +724,18 @@ def test_splitk_deterministic(env):
                                np.zeros(M * N, np.float32), N)
     rep = oracle.bound_check(outs[0], ref[0], S[0], np.zeros((M, N), np.float32), 1.0, 0.0, K)
     assert rep.ok, rep
+
+
+def test_splitk_batch_beyond_one_launch(env):
+    """33000 items x 2 slices are more workgroup rows than one launch takes
+    (65535): the split launches are chunked in whole items and the reduction
+    still sees every item."""
+    M, N, K, batch = 8, 12, 600, 33000
+    w = Workload("skbig", 0, 1, M, N, K, 1.0, 2.0, seed=77, dist="int3", batch=batch)
+    A, B, C = workloads.make_inputs(w)
+    log(f"[split-K chunked] {M}x{N}x{K} batch {batch}")
+    st, got = run_gpu_ws(env, w, A, B, C, variant=2, splits=2, ws_floats=2 * M * N * batch)
+    assert st == 0
+    check_against_oracle(w, A, B, C, got, exact=True, batches=(0, 40))
+    check_against_oracle(w, A, B, C, got, exact=True, batches=(32760, 32800))
+    check_against_oracle(w, A, B, C, got, exact=True, batches=(batch - 40, batch))
