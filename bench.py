@@ -12,10 +12,13 @@ run on (torch's current stream, which is the one passed to the library).
 Every step is one kernel launch, so the timed region over K is also the
 average launch duration used for the roofline figure.
 
+After the timed region one more launch on the pristine inputs must reproduce
+the first launch's output bit for bit (``determinism``).
+
 Prints one JSON line. ``value`` is GFLOP/s (2*M*N*K per GEMM over the timed
 wall time). ``roofline`` reports the same kernel against the FP32-MFMA peak;
 ``traffic`` (HBM bytes per launch) is read from the committed rocprofv3
-counter summary if that summary was taken on the current kernel source, else
+counter summary if that summary was taken on the current kernel code, else
 null. ``cpu_baseline`` times the CPU oracle on a bounded sample of the same
 workload (a band of output rows) on this host's cores.
 """
@@ -25,6 +28,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -37,10 +41,14 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
 def kernel_source_hash() -> str:
-    h = hashlib.sha256()
-    with open(os.path.join(ROOT, "precision_gemm_amd", "csrc", "sgemm.hip"), "rb") as f:
-        h.update(f.read())
-    return h.hexdigest()[:16]
+    """Hash of the kernel source's code: comments and whitespace are dropped,
+    so editing a comment keeps the counter summary current, while any change
+    to the code retires it."""
+    with open(os.path.join(ROOT, "precision_gemm_amd", "csrc", "sgemm.hip")) as f:
+        src = f.read()
+    src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", " ", src)
+    return hashlib.sha256(" ".join(src.split()).encode()).hexdigest()[:16]
 
 
 def load_traffic(workload: str):
@@ -169,7 +177,7 @@ def main(argv=None) -> int:
     # First launch on pristine inputs: its output is what the oracle sample checks.
     step()
     torch.cuda.synchronize(dev)
-    first_out = dC.cpu().numpy() if not args.no_cpu_baseline else None
+    first_out = dC.cpu().numpy()
 
     # Untimed warm-up: the requested W steps, continued until the clock has
     # had min_warmup_ms to ramp up (the first launches run well below the
@@ -197,6 +205,13 @@ def main(argv=None) -> int:
     torch.cuda.synchronize(dev)
 
     total_ms = region0.elapsed_time(region1)
+
+    # Determinism: after the timed launches, one more launch on the pristine
+    # inputs must reproduce the first launch's output bit for bit.
+    dC.copy_(torch.from_numpy(C).to(dev))
+    step()
+    torch.cuda.synchronize(dev)
+    identical = bool((dC.cpu().numpy().view("u4") == first_out.view("u4")).all())
     ms_per_step = total_ms / K
     per_launch_ms = ms_per_step
     flops = w.flops()
@@ -246,6 +261,8 @@ def main(argv=None) -> int:
             "hbm_gbs_at_achieved": round(w.algorithmic_bytes() / (per_launch_ms * 1e-3) / 1e9, 1),
             "kernel_ms": round(per_launch_ms, 5),
         },
+        "determinism": {"rerun_identical_bits": identical},
+        "software": {"torch": torch.__version__, "hip": getattr(torch.version, "hip", None)},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

@@ -41,6 +41,11 @@
 //   * Workgroups are consecutive-ID round-robin over the 8 XCDs; tile IDs are
 //     remapped so that each XCD (and its L2) gets a contiguous run of tiles,
 //     which are then ordered in groups of GROUP_M tile rows.
+//   * Too few tiles to occupy the GPU: the K-split tile runs two wave groups
+//     that share each LDS stage and take half its k-groups each (their
+//     partial tiles meet in LDS at the end); the split-K entry points cut K
+//     across workgroups into a caller workspace and add the slices in a
+//     second kernel, always in slice order, so results stay deterministic.
 
 #include <hip/hip_runtime.h>
 
@@ -573,17 +578,18 @@ sgemm_mfma_kernel(Params p)
 }
 
 // ---------------------------------------------------------------------------
-// Streaming kernel for few, deep tiles (a skinny N, or a grid too small to give
-// every CU a large tile; never launched with split-K): a 64 x 64 tile per workgroup whose four waves each
-// own every fourth K-step (wave w takes steps w, w+4, ...) and accumulate the
-// whole tile over their steps. Every wave fills its own ring of STAGES LDS
-// buffers with direct-to-LDS 16-byte buffer loads (buffer_load_dwordx4 ... lds:
-// lane i of an instruction writes the i-th 16 bytes of a 1 KiB block, an
-// out-of-range lane writes zeros) and reads back only what it loaded itself,
-// so the K loop needs no barrier: a wave waits on its own vmcnt only. Loads run
-// STAGES-1 steps ahead, which keeps enough bytes in flight per CU to stream A
-// at HBM rate. At the end the four partial tiles are summed through LDS in a
-// fixed order (deterministic) and the alpha/beta epilogue is applied.
+// Streaming kernel for a skinny dimension over a deep K whose long operand
+// streams from HBM (never launched with split-K): a 64 x 64 tile per
+// workgroup whose WAVES waves each own every WAVES-th K-step (wave w takes
+// steps w, w+WAVES, ...) and accumulate the whole tile over their steps. Every
+// wave fills its own ring of STAGES LDS buffers with direct-to-LDS 16-byte
+// buffer loads (buffer_load_dwordx4 ... lds: lane i of an instruction writes
+// the i-th 16 bytes of a 1 KiB block, an out-of-range lane writes zeros) and
+// reads back only what it loaded itself, so the K loop needs no barrier: a
+// wave waits on its own vmcnt only. Loads run STAGES-1 steps ahead, which
+// keeps enough bytes in flight per CU to stream the long operand at HBM rate.
+// At the end the partial tiles are summed through LDS in a fixed order
+// (deterministic) and the alpha/beta epilogue is applied.
 // ---------------------------------------------------------------------------
 template <bool KC, int BO, int BK>
 struct DmaOperand {
