@@ -13,7 +13,9 @@ Every step is one kernel launch, so the timed region over K is also the
 average launch duration used for the roofline figure.
 
 After the timed region one more launch on the pristine inputs must reproduce
-the first launch's output bit for bit (``determinism``).
+the first launch's output bit for bit (``determinism``), and ``cold`` times
+single launches after restoring C and flushing L2 and the Infinity Cache with a
+1 GiB fill (median and min; a supplement, not the headline).
 
 Prints one JSON line. ``value`` is GFLOP/s (2*M*N*K per GEMM over the timed
 wall time). ``roofline`` reports the same kernel against the FP32-MFMA peak;
@@ -140,6 +142,9 @@ def main(argv=None) -> int:
                          "(the GPU clock takes tens of ms to ramp up under load)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate CPU time for the oracle baseline sample")
+    ap.add_argument("--cold-launches", type=int, default=20,
+                    help="single launches timed after restoring C and flushing the caches "
+                         "(reported as `cold`, not the headline; 0 skips them)")
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the oracle leg (profiling runs)")
     ap.add_argument("--copy-mib", type=int, default=0,
@@ -212,6 +217,30 @@ def main(argv=None) -> int:
     step()
     torch.cuda.synchronize(dev)
     identical = bool((dC.cpu().numpy().view("u4") == first_out.view("u4")).all())
+
+    # Cold launches (not the headline): before each one C is restored and a
+    # 1 GiB fill evicts L2 and the Infinity Cache, so A, B and C come from HBM;
+    # each launch is timed on its own by an event pair.
+    cold = None
+    if args.cold_launches > 0:
+        pristine = torch.from_numpy(C).to(dev)
+        flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        pairs = []
+        for _ in range(args.cold_launches):
+            dC.copy_(pristine)
+            flush.fill_(1.0)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            step()
+            e1.record(stream)
+            pairs.append((e0, e1))
+        torch.cuda.synchronize(dev)
+        cold_ms = sorted(a.elapsed_time(b) for a, b in pairs)
+        med = cold_ms[len(cold_ms) // 2]
+        cold = {"launches": len(cold_ms), "median_ms": round(med, 5),
+                "min_ms": round(cold_ms[0], 5),
+                "median_tflops": round(w.flops() / (med * 1e-3) / 1e12, 3)}
+        del flush, pristine
     ms_per_step = total_ms / K
     per_launch_ms = ms_per_step
     flops = w.flops()
@@ -262,6 +291,7 @@ def main(argv=None) -> int:
             "kernel_ms": round(per_launch_ms, 5),
         },
         "determinism": {"rerun_identical_bits": identical},
+        "cold": cold,
         "software": {"torch": torch.__version__, "hip": getattr(torch.version, "hip", None)},
         "cpu_baseline": None,
     }
