@@ -107,7 +107,9 @@ enum sgemm_variant {
     SGEMM_VARIANT_L256x256 = 5, /* 256 x 256 tile, 8 waves (two per SIMD in one workgroup) */
     SGEMM_VARIANT_S64x64_K2 = 6,/*  64 x  64 tile, 8 waves: two groups of 4 split each
                                     32-deep K-step, partial tiles added in LDS */
-    SGEMM_VARIANT_COUNT = 7
+    SGEMM_VARIANT_M128x128_DMA = 7,/* 128 x 128 tile, 4 waves, direct-to-LDS loads into a
+                                      3-stage LDS ring */
+    SGEMM_VARIANT_COUNT = 8
 };
 
 /*

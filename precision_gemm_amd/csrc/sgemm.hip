@@ -306,6 +306,55 @@ __device__ __forceinline__ void tile_of(const Params &p, int &b, int &tm, int &t
     tn = (t % in_group) / gsize;
 }
 
+// Epilogue of a tile kernel: C = alpha * res + beta * C for this wave's
+// outputs, lanes outside M x N dropped (C is not read when beta == 0).
+// res[i][j][vv] is accumulator register v0 + vv of the wave's MFMA tile (i, j):
+// register v of lane l holds row 8*(v/4) + 4*(l/32) + v%4, column l%32 of the
+// 32 x 32 product at (wm0 + 32 i, wn0 + 32 j) inside the workgroup tile.
+template <int TM, int TN, int VN>
+__device__ __forceinline__ void store_tile(const Params &p, float *Cb, int m0, int n0, int wm0,
+                                           int wn0, int v0, int lane,
+                                           const float (&res)[TM][TN][VN])
+{
+    const long long cbase = (long long)m0 * p.ldc + n0;
+    const __amdgpu_buffer_rsrc_t rc =
+        make_rsrc(Cb + cbase, (long long)(p.M - 1) * p.ldc + p.N - cbase);
+    const int g = lane >> 5;
+    auto epilogue = [&](auto with_beta) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+                const int col = wn0 + 32 * j + (lane & 31);
+                const bool col_ok = n0 + col < p.N;
+                uint32_t off[VN];
+                float c[VN];
+#pragma unroll
+                for (int vv = 0; vv < VN; ++vv) {
+                    const int v = v0 + vv;
+                    const int row = wm0 + 32 * i + 8 * (v >> 2) + 4 * g + (v & 3);
+                    off[vv] = (col_ok && m0 + row < p.M)
+                                  ? (uint32_t)(((long long)row * p.ldc + col) * 4)
+                                  : kOOB;
+                    if (with_beta)
+                        c[vv] = load1(rc, off[vv]);
+                }
+#pragma unroll
+                for (int vv = 0; vv < VN; ++vv) {
+                    float out = p.alpha * res[i][j][vv];
+                    if (with_beta)
+                        out += p.beta * c[vv];
+                    store1(rc, off[vv], out);
+                }
+            }
+        }
+    };
+    if (p.beta != 0.0f)
+        epilogue(std::true_type{});
+    else
+        epilogue(std::false_type{});
+}
+
 // WAVES_K = 2 splits every K-step between two groups of WAVES_M x WAVES_N
 // waves: group g multiplies the k-groups [g*NQ/2, (g+1)*NQ/2) of each stage
 // into its own accumulators, which gives every SIMD two waves on a tile that
@@ -537,44 +586,7 @@ sgemm_mfma_kernel(Params p)
                 }
     }
 
-    // Epilogue: C = alpha * acc + beta * C, lanes outside M x N dropped.
-    const long long cbase = (long long)m0 * p.ldc + n0;
-    const __amdgpu_buffer_rsrc_t rc =
-        make_rsrc(Cb + cbase, (long long)(p.M - 1) * p.ldc + p.N - cbase);
-    const int g = lane >> 5;
-    auto epilogue = [&](auto with_beta) {
-#pragma unroll
-        for (int i = 0; i < TM; ++i) {
-#pragma unroll
-            for (int j = 0; j < TN; ++j) {
-                const int col = wn0 + 32 * j + (lane & 31);
-                const bool col_ok = n0 + col < p.N;
-                uint32_t off[VN];
-                float c[VN];
-#pragma unroll
-                for (int vv = 0; vv < VN; ++vv) {
-                    const int v = v0 + vv;
-                    const int row = wm0 + 32 * i + 8 * (v >> 2) + 4 * g + (v & 3);
-                    off[vv] = (col_ok && m0 + row < p.M)
-                                  ? (uint32_t)(((long long)row * p.ldc + col) * 4)
-                                  : kOOB;
-                    if (with_beta)
-                        c[vv] = load1(rc, off[vv]);
-                }
-#pragma unroll
-                for (int vv = 0; vv < VN; ++vv) {
-                    float out = p.alpha * res[i][j][vv];
-                    if (with_beta)
-                        out += p.beta * c[vv];
-                    store1(rc, off[vv], out);
-                }
-            }
-        }
-    };
-    if (p.beta != 0.0f)
-        epilogue(std::true_type{});
-    else
-        epilogue(std::false_type{});
+    store_tile<TM, TN, VN>(p, Cb, m0, n0, wm0, wn0, v0, lane, res);
 }
 
 // ---------------------------------------------------------------------------
@@ -591,18 +603,23 @@ sgemm_mfma_kernel(Params p)
 // At the end the partial tiles are summed through LDS in a fixed order
 // (deterministic) and the alpha/beta epilogue is applied.
 // ---------------------------------------------------------------------------
-template <bool KC, int BO, int BK>
+// NW waves share each K-step tile: wave w loads blocks w, w + NW, ... (NW = 1:
+// a wave loads its whole tile).
+template <bool KC, int BO, int BK, int NW = 1>
 struct DmaOperand {
     static constexpr int FLOATS = BO * BK;         // one K-step tile
     static constexpr int NINST = FLOATS * 4 / 1024; // 1 KiB blocks, one load instruction each
+    static constexpr int NBW = NINST / NW;          // blocks loaded by each wave
     static constexpr int C4 = KC ? BK / 4 : BO / 4; // 16-byte chunks per stored row of the tile
     static constexpr int SWZ_ROWS = BK >= 64 ? 1 : 64 / BK;
     static_assert(FLOATS * 4 % 1024 == 0, "tile must be whole 1 KiB blocks");
+    static_assert(NINST % NW == 0, "blocks must split evenly over the waves");
 
     const float *X;
     long long ld, total;
     int O, K, o0;
-    uint32_t off[NINST]; // this lane's chunk in block b, relative to the step's window
+    int wv;               // this wave's index among the NW sharing the tile
+    uint32_t off[NBW];    // this lane's chunk in each of its blocks, relative to the step's window
     // Window of this wave's next K-step (the waves of a workgroup take every
     // WAVES-th step): first element and first k, and its buffer range kept as
     // in Operand (`big` windows capped at 2^31 - 1, then `rem` exact bytes).
@@ -624,14 +641,15 @@ struct DmaOperand {
     }
 
     // k0: first k of this wave's first step; kstride: k between its steps.
-    __device__ __forceinline__ void init(int lane, int k0, int kstride)
+    __device__ __forceinline__ void init(int lane, int k0, int kstride, int wave_in_tile = 0)
     {
+        wv = wave_in_tile;
 #pragma unroll
-        for (int b = 0; b < NINST; ++b) {
+        for (int i = 0; i < NBW; ++i) {
             int r, c;
-            chunk(b, lane, r, c);
+            chunk(wv + NW * i, lane, r, c);
             const bool ok = KC ? (o0 + r < O) : (o0 + 4 * c < O);
-            off[b] = ok ? (uint32_t)(((long long)r * ld + 4 * c) * 4) : kOOB;
+            off[i] = ok ? (uint32_t)(((long long)r * ld + 4 * c) * 4) : kOOB;
         }
         const long long base = KC ? (long long)o0 * ld + k0 : (long long)k0 * ld + o0;
         wp = X + base;
@@ -659,8 +677,9 @@ struct DmaOperand {
         const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
             const_cast<float *>(wp), (short)0, (int)range, kRsrcWord3);
 #pragma unroll
-        for (int b = 0; b < NINST; ++b) {
-            uint32_t o = off[b];
+        for (int i = 0; i < NBW; ++i) {
+            const int b = wv + NW * i;
+            uint32_t o = off[i];
             if (TAIL) {
                 int r, c;
                 chunk(b, lane, r, c);
@@ -896,6 +915,203 @@ sgemm_stream_kernel(Params p)
     }
 }
 
+// ---------------------------------------------------------------------------
+// Tile kernel with direct-to-LDS staging: the tile, wave layout, LDS layout,
+// fragment reads and epilogue of sgemm_mfma_kernel (WAVES_K = 1), but every
+// K-step tile goes from global memory straight into LDS with buffer_load ...
+// lds. Wave w issues the 1 KiB blocks w, w + NW, ... of each operand's tile,
+// so no registers stage the data and no LDS write instructions are issued.
+// Three LDS stages form a ring: at the start of step s the loads of step s+2
+// go into the stage step s-1 occupied (every wave finished reading it before
+// the barrier that ended step s-1). At the end of step s each wave waits until
+// only its step s+2 loads are in flight (vector-memory operations complete in
+// issue order), and the barrier then publishes step s+1 to all waves. The
+// loads stop at the last step, so none is pending when the workgroup ends.
+// ---------------------------------------------------------------------------
+template <int BM, int BN, int WAVES_M, int WAVES_N, int MIN_WAVES_PER_EU, bool A_KC, bool B_KC,
+          bool EVEN_K>
+__global__ void
+__attribute__((amdgpu_flat_work_group_size(64 * WAVES_M * WAVES_N, 64 * WAVES_M * WAVES_N),
+               amdgpu_waves_per_eu(MIN_WAVES_PER_EU)))
+sgemm_dma_kernel(Params p)
+{
+    constexpr int BK = 16, NW = WAVES_M * WAVES_N, NT = 64 * NW;
+    constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N, TM = WM / 32, TN = WN / 32;
+    constexpr int NQ = BK / 8, LATE = TM * TN;
+    using FA = Operand<A_KC, BM, BK, NT, 4>; // LDS layout and fragment reads
+    using FB = Operand<B_KC, BN, BK, NT, 4>;
+    using DA = DmaOperand<A_KC, BM, BK, NW>;
+    using DB = DmaOperand<B_KC, BN, BK, NW>;
+    static_assert(FA::STAGE == DA::FLOATS && FB::STAGE == DB::FLOATS, "one layout");
+    constexpr int STAGE = FA::STAGE + FB::STAGE;
+    constexpr int NI = DA::NBW + DB::NBW; // load instructions per wave and step
+    static_assert(NI <= 63, "vmcnt holds at most 63");
+    __shared__ __attribute__((aligned(16))) float lds[3 * STAGE];
+
+    int b, tile_m, tile_n;
+    tile_of(p, b, tile_m, tile_n);
+    const int m0 = tile_m * BM, n0 = tile_n * BN;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wm0 = (wave % WAVES_M) * WM, wn0 = (wave / WAVES_M) * WN;
+
+    // K range of this workgroup, as in sgemm_mfma_kernel.
+    int item = b, k0 = 0, Kt = p.K;
+    if (p.splits > 1) {
+        item = b / p.splits;
+        k0 = (b - item * p.splits) * p.kslice;
+        Kt = min(p.kslice, p.K - k0);
+    }
+    const float *Ab = item_a(p, item) + (A_KC ? (long long)k0 : (long long)k0 * p.lda);
+    const float *Bb = item_b(p, item) + (B_KC ? (long long)k0 : (long long)k0 * p.ldb);
+    float *Cb = item_c(p, b);
+    if (((uintptr_t)Ab | (uintptr_t)Bb) & 15u) {
+        plain_tile<BM, BN, NT, A_KC, B_KC>(p, Ab, Bb, Cb, Kt, m0, n0);
+        return;
+    }
+
+    DA da;
+    da.X = Ab;
+    da.ld = p.lda;
+    da.total = A_KC ? (long long)(p.M - 1) * p.lda + Kt : (long long)(Kt - 1) * p.lda + p.M;
+    da.O = p.M;
+    da.K = Kt;
+    da.o0 = m0;
+    da.init(lane, 0, BK, wave);
+    DB db;
+    db.X = Bb;
+    db.ld = p.ldb;
+    db.total = B_KC ? (long long)(p.N - 1) * p.ldb + Kt : (long long)(Kt - 1) * p.ldb + p.N;
+    db.O = p.N;
+    db.K = Kt;
+    db.o0 = n0;
+    db.init(lane, 0, BK, wave);
+
+    f32x16 acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+            acc[i][j] = f32x16{};
+
+    const int nsteps = (Kt + BK - 1) / BK;
+    auto issue = [&](float *stage, auto tail) {
+        da.template issue<decltype(tail)::value>(stage, lane);
+        db.template issue<decltype(tail)::value>(stage + FA::STAGE, lane);
+    };
+    auto read_group = [&](const float *stage, int q, float (&fa)[TM][4], float (&fb)[TN][4]) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+            FA::frag(stage, wm0 + 32 * i, q, lane, fa[i]);
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+            FB::frag(stage + FA::STAGE, wn0 + 32 * j, q, lane, fb[j]);
+    };
+    auto mfma_group = [&](const float (&fa)[TM][4], const float (&fb)[TN][4], int first, int last) {
+#pragma unroll
+        for (int t = 0; t < 4 * TM * TN; ++t) {
+            if (t < first || t >= last)
+                continue;
+            const int kk = t / (TM * TN), i = (t / TN) % TM, j = t % TN;
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[i][kk], fb[j][kk], acc[i][j],
+                                                              0, 0, 0);
+        }
+    };
+
+    // Steps 0 and 1 into stages 0 and 1; wait for step 0.
+    using Tail = std::bool_constant<!EVEN_K>;
+    issue(lds, Tail{});
+    if (nsteps > 1) {
+        issue(lds + STAGE, Tail{});
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(NI));
+    } else {
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    }
+    __syncthreads();
+    float fa[NQ][TM][4], fb[NQ][TN][4];
+    read_group(lds, 0, fa[0], fb[0]);
+
+    // Step s in stage STG = s % 3. MODE 0 issues step s+2 without the k mask,
+    // 1 with it (it may be the partial last step), 2 issues nothing (s+2 is
+    // past the last step).
+    auto k_step = [&](auto stg, auto mode) {
+        constexpr int STG = decltype(stg)::value, MODE = decltype(mode)::value;
+        const float *cur = lds + STG * STAGE;
+        const float *nxt = lds + ((STG + 1) % 3) * STAGE;
+        float *ahead = lds + ((STG + 2) % 3) * STAGE;
+        if constexpr (MODE == 0)
+            issue(ahead, std::false_type{});
+        else if constexpr (MODE == 1)
+            issue(ahead, std::true_type{});
+#pragma unroll
+        for (int q = 1; q < NQ; ++q)
+            read_group(cur, q, fa[q], fb[q]);
+        mfma_group(fa[0], fb[0], 0, 4 * TM * TN);
+#pragma unroll
+        for (int q = 1; q < NQ - 1; ++q)
+            mfma_group(fa[q], fb[q], 0, 4 * TM * TN);
+        mfma_group(fa[NQ - 1], fb[NQ - 1], 0, 4 * TM * TN - LATE);
+        // Order: the loads, this stage's remaining fragment reads, the MFMAs.
+        if constexpr (MODE != 2)
+            __builtin_amdgcn_sched_group_barrier(0x020, NI, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 4 * (TM + TN) * (NQ - 1), 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 4 * TM * TN * NQ - LATE, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (MODE == 2)
+            __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+        else
+            __builtin_amdgcn_s_waitcnt(waitcnt_vm(NI));
+        __syncthreads();
+        __builtin_amdgcn_sched_barrier(0);
+        // (After the last step this reads a stage whose values are unused.)
+        read_group(nxt, 0, fa[0], fb[0]);
+        mfma_group(fa[NQ - 1], fb[NQ - 1], 4 * TM * TN - LATE, 4 * TM * TN);
+        __builtin_amdgcn_sched_group_barrier(0x100, 4 * (TM + TN), 0); // LDS reads
+        __builtin_amdgcn_sched_group_barrier(0x008, LATE, 0);          // MFMAs
+    };
+    using S0 = std::integral_constant<int, 0>;
+    using S1 = std::integral_constant<int, 1>;
+    using S2 = std::integral_constant<int, 2>;
+    using Plain = std::integral_constant<int, 0>;
+    using Masked = std::integral_constant<int, 1>;
+    using NoLoad = std::integral_constant<int, 2>;
+    // Steps before `steady` issue unmasked loads: all with s + 2 < nsteps if
+    // K is a multiple of BK, else all but the one issuing the last step.
+    const int steady = EVEN_K ? nsteps - 2 : nsteps - 3;
+    int s = 0;
+    for (; s + 3 <= steady; s += 3) {
+        k_step(S0{}, Plain{});
+        k_step(S1{}, Plain{});
+        k_step(S2{}, Plain{});
+    }
+    // The rest, s % 3 == 0 at entry: one copy per (stage, mode).
+    auto any_step = [&](auto stg, int st) {
+        if (st < steady)
+            k_step(stg, Plain{});
+        else if (st + 2 < nsteps)
+            k_step(stg, Masked{});
+        else
+            k_step(stg, NoLoad{});
+    };
+    for (; s < nsteps; s += 3) {
+        any_step(S0{}, s);
+        if (s + 1 < nsteps)
+            any_step(S1{}, s + 1);
+        if (s + 2 < nsteps)
+            any_step(S2{}, s + 2);
+    }
+
+    float res[TM][TN][16];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v)
+                res[i][j][v] = acc[i][j][v];
+    store_tile<TM, TN, 16>(p, Cb, m0, n0, wm0, wn0, 0, lane, res);
+}
+
 // C = beta * C over the M x N window of every batch item (alpha == 0 or K == 0).
 __global__ void __launch_bounds__(256) sgemm_scale_kernel(float *C, float *const *Carr, int M,
                                                           int N, int ldc, long long sC,
@@ -964,6 +1180,20 @@ constexpr VariantInfo make_variant()
            sgemm_mfma_kernel<BM, BN, BK, WM_, WN_, WK_, MW, false, true, true, VEC>}}}};
 }
 
+template <int BM, int BN, int WM_, int WN_, int MW>
+constexpr VariantInfo make_dma_variant()
+{
+    return VariantInfo{BM, BN, 16, 64 * WM_ * WN_, 4,
+                       {{{sgemm_dma_kernel<BM, BN, WM_, WN_, MW, true, false, false>,
+                          sgemm_dma_kernel<BM, BN, WM_, WN_, MW, true, false, true>},
+                         {sgemm_dma_kernel<BM, BN, WM_, WN_, MW, true, true, false>,
+                          sgemm_dma_kernel<BM, BN, WM_, WN_, MW, true, true, true>}},
+                        {{sgemm_dma_kernel<BM, BN, WM_, WN_, MW, false, false, false>,
+                          sgemm_dma_kernel<BM, BN, WM_, WN_, MW, false, false, true>},
+                         {sgemm_dma_kernel<BM, BN, WM_, WN_, MW, false, true, false>,
+                          sgemm_dma_kernel<BM, BN, WM_, WN_, MW, false, true, true>}}}};
+}
+
 template <int WAVES, int STAGES>
 constexpr VariantInfo make_stream_variant()
 {
@@ -986,6 +1216,7 @@ const VariantInfo kVariants[SGEMM_VARIANT_COUNT] = {
     make_stream_variant<4, 4>(),                  // SGEMM_VARIANT_T64x64
     make_variant<256, 256, kBK, 2, 4, 1, 2, 4>(), // SGEMM_VARIANT_L256x256
     make_variant<64, 64, 32, 2, 2, 2, 2, 4>(),    // SGEMM_VARIANT_S64x64_K2
+    make_dma_variant<128, 128, 2, 2, 2>(),        // SGEMM_VARIANT_M128x128_DMA
 };
 
 long long ceil_div(long long a, long long b) { return (a + b - 1) / b; }
@@ -1072,8 +1303,8 @@ extern "C" int sgemm_select_variant(int transA, int transB, int M, int N, int K,
     // relative efficiency. The efficiencies are fitted to a sweep of every
     // variant over 24 shapes (precision_gemm_amd/tune.py): 128 x 128 tiles
     // 1.00; the K-split 64 x 64 tile 0.88, for K >= 768; plain 64 x 64 tiles
-    // 0.85. The 256-row tiles never won by more than the sweep's noise, so
-    // they are left to explicit requests.
+    // 0.85. The 256-row tiles and the direct-to-LDS 128 x 128 tile never won
+    // by more than the sweep's noise, so they are left to explicit requests.
     struct Choice { int variant, bm, bn, eff_pct; long long min_k; };
     const Choice choices[] = {{SGEMM_VARIANT_M128x128, 128, 128, 100, 0},
                               {SGEMM_VARIANT_S64x64_K2, 64, 64, 88, 768},

@@ -477,7 +477,7 @@ def test_pointer_array_bitwise(env, variant):
         check_items(tA, tB, M, N, K, 2.0, -1.0, lda, ldb, ldc, res, exact=True)
 
 
-@pytest.mark.parametrize("variant", [-1, 0, 2, 4, 5, 6])
+@pytest.mark.parametrize("variant", [-1, 0, 2, 4, 5, 6, 7])
 def test_pointer_array_misaligned_items(env, variant):
     """Items whose A or B is not 16-byte aligned, in a launch of a 4-float
     kernel: those items take the kernel's plain per-element path and must
