@@ -220,3 +220,50 @@ def test_workspace_size_without_a_device(pg):
     # no device to query here: the size is 0 (and invalid shapes are always 0)
     assert pg.sgemm_workspace_size(0, 0, 256, 256, 16384, 1) >= 0
     assert pg.sgemm_workspace_size(0, 0, -1, 256, 16384, 1) == 0
+
+
+# ------------------------------------------------------------------ properties of the host decisions
+
+from hypothesis import given, settings, strategies as st  # noqa: E402
+
+_dim = st.integers(min_value=1, max_value=1 << 16)
+
+
+@settings(max_examples=300, deadline=None)
+@given(tA=st.integers(0, 1), tB=st.integers(0, 1), M=_dim, N=_dim, K=_dim,
+       batch=st.integers(1, 512), vec4=st.booleans(), cus=st.integers(1, 512))
+def test_select_variant_is_always_a_kernel(pg, tA, tB, M, N, K, batch, vec4, cus):
+    """Any valid shape gets a variant in range; without 4-float loads it is the
+    1-float variant; the streaming kernel only for a dimension of at most 64."""
+    v = pg.sgemm_select_variant(tA, tB, M, N, K, batch, vec4, cus)
+    assert 0 <= v < pg.VARIANT_COUNT
+    if not vec4:
+        assert v == pg.VARIANT_S64x64_V1
+    if v == pg.VARIANT_T64x64:
+        assert min(M, N) <= 64 and K >= 512
+    assert v not in (pg.VARIANT_L256x128, pg.VARIANT_L256x256, pg.VARIANT_M128x128_DMA)
+
+
+@settings(max_examples=300, deadline=None)
+@given(M=_dim, N=_dim, K=st.integers(1, 1 << 22), batch=st.integers(1, 64),
+       variant=st.sampled_from([0, 1, 2, 3, 5, 6, 7]), cus=st.integers(1, 512))
+def test_select_splits_covers_k_exactly(pg, M, N, K, batch, variant, cus):
+    """The split count S is in [1, 128]; the slices of round_up(ceil(K/S), BK)
+    k cover K with no empty slice; a split only happens with slices at least
+    256 deep."""
+    S = pg.sgemm_select_splits(0, 0, M, N, K, batch, variant, cus)
+    assert 1 <= S <= 128
+    if S == 1:
+        return
+    bk = 32 if variant == pg.VARIANT_S64x64_K2 else 16
+    # the slice length the library uses for this S (the count it returns is
+    # already that of the non-empty slices)
+    ks = None
+    for s0 in range(S, 129):
+        cand = -(-(-(-K // s0)) // bk) * bk
+        if -(-K // cand) == S:
+            ks = cand
+            break
+    assert ks is not None
+    assert ks % bk == 0 and (S - 1) * ks < K <= S * ks
+    assert K // S >= 128   # slices are never thin (at least ~256 deep before rounding)
