@@ -1300,15 +1300,18 @@ extern "C" int sgemm_select_variant(int transA, int transB, int M, int N, int K,
         return SGEMM_VARIANT_T64x64;
     // Otherwise the tile whose busiest CU finishes first: a CU receives
     // ceil(tiles / CUs) tiles, each costing its area over the variant's
-    // relative efficiency. The efficiencies are fitted to a sweep of every
-    // variant over 24 shapes (precision_gemm_amd/tune.py): 128 x 128 tiles
+    // relative efficiency. The efficiencies are fitted to sweeps of every
+    // variant over 48 shapes (precision_gemm_amd/tune.py): 128 x 128 tiles
     // 1.00; the K-split 64 x 64 tile 0.88, for K >= 768; plain 64 x 64 tiles
-    // 0.85. The 256-row tiles and the direct-to-LDS 128 x 128 tile never won
-    // by more than the sweep's noise, so they are left to explicit requests.
+    // 0.85, or 1.05 for K <= 512, where a tile's fixed costs (the first loads,
+    // the C stores) outweigh its short K loop and the small tiles, more of
+    // them resident per CU, overlap those costs better. The 256-row tiles and
+    // the direct-to-LDS 128 x 128 tile never won by more than the sweeps'
+    // noise on the shapes that matter, so they are left to explicit requests.
     struct Choice { int variant, bm, bn, eff_pct; long long min_k; };
     const Choice choices[] = {{SGEMM_VARIANT_M128x128, 128, 128, 100, 0},
                               {SGEMM_VARIANT_S64x64_K2, 64, 64, 88, 768},
-                              {SGEMM_VARIANT_S64x64, 64, 64, 85, 0}};
+                              {SGEMM_VARIANT_S64x64, 64, 64, K <= 512 ? 105 : 85, 0}};
     int best = SGEMM_VARIANT_S64x64;
     double best_cost = -1.0;
     for (const Choice &c : choices) {

@@ -1,7 +1,7 @@
 """Dispatch sweep: time every kernel variant on a grid of shapes and report how
 far the library's automatic choice is from the fastest one.
 
-    python -m precision_gemm_amd.tune [--shapes default|quick] [--json out.json]
+    python -m precision_gemm_amd.tune [--shapes default|quick|wide] [--json out.json]
     python -m precision_gemm_amd.tune --splitk [--json out.json]
 
 For each shape every applicable variant is timed on the same device buffers,
@@ -53,6 +53,22 @@ DEFAULT_SHAPES = [
     (1, 1, 16384, 64, 4096, 1, 0.0),
 ]
 QUICK_SHAPES = [DEFAULT_SHAPES[i] for i in (3, 6, 10, 16, 19)]
+# Shapes the cost model was not fitted on: non-square, every transpose pair,
+# odd sizes, short K, batches.
+WIDE_SHAPES = [
+    (1, 0, 4096, 4096, 4096, 1, 0.0), (0, 1, 4096, 4096, 4096, 1, 1.0),
+    (1, 1, 4096, 4096, 4096, 1, 0.0), (0, 0, 3000, 3000, 3000, 1, 0.0),
+    (0, 0, 5000, 5000, 5000, 1, 0.5), (1, 0, 2000, 3000, 1000, 1, 0.0),
+    (0, 0, 8192, 1024, 4096, 1, 0.0), (0, 0, 1024, 8192, 4096, 1, 0.0),
+    (0, 1, 16384, 512, 2048, 1, 0.0), (0, 0, 512, 16384, 2048, 1, 0.0),
+    (0, 0, 4096, 4096, 256, 1, 0.0), (0, 0, 8192, 8192, 128, 1, 1.0),
+    (0, 0, 2048, 2048, 64, 1, 0.0), (0, 0, 1536, 1536, 4096, 1, 0.0),
+    (0, 0, 2304, 2304, 2304, 1, 0.0), (0, 0, 3584, 3584, 3584, 1, 0.0),
+    (1, 0, 256, 256, 1024, 256, 0.0), (0, 1, 128, 128, 2048, 512, 0.0),
+    (0, 0, 1024, 1024, 1024, 16, 0.0), (0, 0, 384, 768, 3072, 32, 0.0),
+    (0, 1, 32768, 128, 4096, 1, 0.0), (0, 0, 128, 32768, 4096, 1, 0.0),
+    (0, 0, 96, 96, 96, 1, 0.0), (0, 0, 640, 480, 2000, 1, 0.0),
+]
 
 
 def time_variant(torch, pg, stream, call, launches: int) -> float:
@@ -216,7 +232,7 @@ def splitk_sweep(shapes, rounds: int = 3, target_ms: float = 20.0, out=sys.stdou
 
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
-    ap.add_argument("--shapes", choices=["default", "quick"], default="default")
+    ap.add_argument("--shapes", choices=["default", "quick", "wide"], default="default")
     ap.add_argument("--splitk", action="store_true",
                     help="compare the plain and split-K automatic calls on deep-K shapes")
     ap.add_argument("--rounds", type=int, default=3)
@@ -228,7 +244,7 @@ def main(argv=None) -> int:
             with open(args.json, "w") as f:
                 json.dump(res, f, indent=1)
         return 0
-    shapes = DEFAULT_SHAPES if args.shapes == "default" else QUICK_SHAPES
+    shapes = {"default": DEFAULT_SHAPES, "quick": QUICK_SHAPES, "wide": WIDE_SHAPES}[args.shapes]
     res = sweep(shapes, rounds=args.rounds)
     regrets = [r["regret"] for r in res]
     print(f"shapes {len(res)}: mean regret {100 * statistics.mean(regrets):.2f} %, "

@@ -130,16 +130,20 @@ def test_select_variant(pg):
     # 6144^3, 8192^3 and the batched 64 x 512^2 workload
     for shape, batch, tA in (((4092, 4092, 4092), 1, 0), ((2048, 2048, 2048), 1, 0),
                              ((6144, 6144, 6144), 1, 0), ((8192, 8192, 8192), 1, 0),
-                             ((512, 512, 520), 64, 1), ((2048, 2048, 512), 1, 0)):
+                             ((512, 512, 520), 64, 1)):
         assert sel(tA, 0, *shape, batch, True, 256) == pg.VARIANT_M128x128, shape
     # few 64 x 64 tiles per CU over K >= 768: the K-split eight-wave tile
     for shape in ((1024, 1024, 1024), (3072, 3072, 3072), (1536, 1536, 1536),
                   (1024, 1024, 4096), (1000, 1000, 1000), (512, 512, 8192)):
         assert sel(0, 0, *shape, 1, True, 256) == pg.VARIANT_S64x64_K2, shape
     assert sel(0, 0, 512, 512, 2048, 8, True, 256) == pg.VARIANT_S64x64_K2
-    # ... and the plain 64 x 64 tile below K = 768
+    # ... and the plain 64 x 64 tile below K = 768; for K <= 512 it also beats
+    # the 128 x 128 tile on full grids (per-tile fixed costs dominate)
     assert sel(0, 0, 512, 512, 512, 1, True, 256) == pg.VARIANT_S64x64
     assert sel(0, 0, 128, 128, 128, 1, True, 256) == pg.VARIANT_S64x64
+    for shape in ((2048, 2048, 512), (4096, 4096, 256), (8192, 8192, 128), (2048, 2048, 64)):
+        assert sel(0, 0, *shape, 1, True, 256) == pg.VARIANT_S64x64, shape
+    assert sel(0, 0, 4096, 4096, 520, 1, True, 256) == pg.VARIANT_M128x128
     # a skinny dimension with a long operand over 128 MiB streams, whatever
     # the transposes; one of at most 128 MiB stays with the tiles
     for tA, tB in ((0, 1), (0, 0), (1, 1), (1, 0)):
