@@ -153,7 +153,7 @@ def main(argv=None) -> int:
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (--gpus {args.gpus} requested); "
+        print(f"bench.py: this benchmark runs on one GPU only (--gpus {args.gpus} requested); "
               "sharding across GPUs is described in the design notes, not run.",
               file=sys.stderr)
         return 2

@@ -71,5 +71,5 @@ def test_mfma_issue_rate(probes):
     sys.stdout.write(f"FP32 MFMA rate {tf.value:.1f} TFLOP/s "
                      f"({100 * tf.value / 157.3:.1f} % of 157.3) on {cus} CUs\n")
     sys.stdout.flush()
-    # a sanity floor only: the rate depends on the clock the box runs at
+    # a sanity floor only: the rate depends on the clock the device runs at
     assert tf.value > 0.5 * 157.3 * cus / 256

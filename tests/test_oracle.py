@@ -345,8 +345,8 @@ def test_workload_shapes_and_counts():
     h = workloads.HEADLINE
     assert h.flops() == 137_036_693_376
     assert h.algorithmic_bytes() == 267_911_424
-    A, B, C = workloads.make_inputs(workloads.CONFIGS[0])
+    A, B, C = workloads.make_inputs(workloads.BY_NAME["sgemm_128"])
     assert A.dtype == np.float32 and A.size == 128 * 128
     assert A.min() >= -1 and A.max() <= 1
-    A2, _, _ = workloads.make_inputs(workloads.CONFIGS[0])
+    A2, _, _ = workloads.make_inputs(workloads.BY_NAME["sgemm_128"])
     np.testing.assert_array_equal(A, A2)
