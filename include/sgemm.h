@@ -50,7 +50,11 @@
  *        position of their `variant` argument; the split-K entry points
  *        return -19 for an invalid split count, -20 for an invalid
  *        workspace and -21 for a workspace too small for a forced split,
- *        whatever the position of those arguments.
+ *        whatever the position of those arguments. Every entry point
+ *        returns -22 when one batch item has more output tiles than one
+ *        kernel launch holds: more than 2^31 - 1 work-items along the tile
+ *        axis (for the 64 x 64 tiles, M x N beyond about 2^34 to 2^35
+ *        elements per item, a C of 64 GiB or more).
  *    >0  a hipError_t raised when querying the device or launching.
  * sgemm_status_string() turns any status into a message.
  *

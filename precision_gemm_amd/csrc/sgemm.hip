@@ -1308,14 +1308,17 @@ extern "C" int sgemm_select_variant(int transA, int transB, int M, int N, int K,
     // them resident per CU, overlap those costs better. The 256-row tiles and
     // the direct-to-LDS 128 x 128 tile never won by more than the sweeps'
     // noise on the shapes that matter, so they are left to explicit requests.
+    // A tile whose grid would not fit one launch (more than 2^31 - 1
+    // work-items per item along the tile axis) is skipped.
     struct Choice { int variant, bm, bn, eff_pct; long long min_k; };
     const Choice choices[] = {{SGEMM_VARIANT_M128x128, 128, 128, 100, 0},
                               {SGEMM_VARIANT_S64x64_K2, 64, 64, 88, 768},
                               {SGEMM_VARIANT_S64x64, 64, 64, K <= 512 ? 105 : 85, 0}};
-    int best = SGEMM_VARIANT_S64x64;
+    int best = SGEMM_VARIANT_M128x128;
     double best_cost = -1.0;
     for (const Choice &c : choices) {
-        if (K < c.min_k)
+        if (K < c.min_k ||
+            ceil_div(M, c.bm) * ceil_div(N, c.bn) * kVariants[c.variant].threads > INT32_MAX)
             continue;
         const long long tiles = ceil_div(M, c.bm) * ceil_div(N, c.bn) * batch;
         const double cost = (double)ceil_div(tiles, cus) * c.bm * c.bn * 100.0 / c.eff_pct;
@@ -1500,6 +1503,12 @@ int launch(const Call &c, int variant, hipStream_t s, Split sk = Split{nullptr, 
     }
 
     const VariantInfo &vi = kVariants[variant];
+    // One launch holds every tile of an item along grid x, and the runtime
+    // counts that axis in work-items (a signed 32-bit range); the tile index
+    // inside the kernels is an int as well.
+    const long long tiles_item = ceil_div(c.M, vi.bm) * ceil_div(c.N, vi.bn);
+    if (tiles_item * vi.threads > INT32_MAX || (long long)splits * tiles_item > INT32_MAX)
+        return -22;
     const int even_k = c.K % vi.bk == 0 ? 1 : 0;
     Params p;
     p.A = c.A;
@@ -1541,9 +1550,7 @@ int launch(const Call &c, int variant, hipStream_t s, Split sk = Split{nullptr, 
     long long max_flat = ((1LL << 31) - 1) / per_batch;
     if (max_flat > 65535)
         max_flat = 65535;
-    max_flat -= max_flat % splits;
-    if (max_flat < 1)
-        return -3;
+    max_flat -= max_flat % splits; // >= splits: splits * per_batch <= INT32_MAX above
     KernelFn fn = vi.fn[c.tA][c.tB][even_k];
     for (long long b0 = 0; b0 < flat; b0 += max_flat) {
         const long long nb = flat - b0 < max_flat ? flat - b0 : max_flat;
@@ -1801,6 +1808,7 @@ extern "C" const char *sgemm_status_string(int status)
     case -19: return "invalid split count (negative, over 65535, or a split of the streaming variant)";
     case -20: return "invalid workspace (NULL or not 4-byte aligned while workspace_bytes > 0)";
     case -21: return "workspace too small for the requested split count";
+    case -22: return "problem too large: one batch item has more output tiles than one launch holds";
     default: break;
     }
     if (status < 0)

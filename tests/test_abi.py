@@ -154,6 +154,10 @@ def test_select_variant(pg):
     assert sel(0, 1, 16384, 64, 128, 1, True, 256) != pg.VARIANT_T64x64
     # the CU count enters the model: on 64 CUs 2048^3 has four 128 x 128 tiles per CU
     assert sel(0, 0, 2048, 2048, 2048, 1, True, 64) == pg.VARIANT_M128x128
+    # a tile whose grid would exceed one launch is passed over: 2^24 tiles of
+    # 64 x 64 (2^32 work-items), while 2^22 tiles of 128 x 128 still fit
+    assert sel(0, 0, 1 << 29, 128, 256, 1, True, 256) == pg.VARIANT_M128x128
+    assert sel(0, 0, 1 << 20, 128, 256, 1, True, 256) == pg.VARIANT_S64x64
     # no 4-float loads: the 1-float variant
     assert sel(0, 0, 4092, 4092, 4092, 1, False, 256) == pg.VARIANT_S64x64_V1
     assert sel(3, 0, 4, 4, 4, 1, True, 256) == -1
@@ -218,6 +222,19 @@ def test_split_arguments_checked(pg):
     for st in (-19, -20, -21):
         assert "invalid" in pg.sgemm_status_string(st) or "too small" in \
             pg.sgemm_status_string(st)
+
+
+def test_oversize_grid_is_rejected(pg):
+    """More output tiles in one item than one launch's tile axis holds (in
+    work-items, a signed 32-bit range) is an error before any device work.
+    Only rejected calls are made here: the pointers are fake."""
+    # 2^22 tiles of 64 x 64 for the 512-thread K-split tile: 2^31 work-items
+    assert ws_call(pg, variant=pg.VARIANT_S64x64_K2, splits=1, M=1 << 28, N=64, K=4, lda=4,
+                   ldb=64, ldc=64) == -22
+    # 2^23 + 1 tiles for the 256-thread streaming tile
+    assert ws_call(pg, variant=pg.VARIANT_T64x64, splits=1, M=((1 << 23) + 1) * 64, N=64, K=4,
+                   lda=4, ldb=64, ldc=64) == -22
+    assert "too large" in pg.sgemm_status_string(-22)
 
 
 def test_workspace_size_without_a_device(pg):
