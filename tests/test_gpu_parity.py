@@ -308,6 +308,75 @@ def test_deterministic(env):
     assert np.array_equal(g1.view(np.uint32), g2.view(np.uint32))
 
 
+def test_concurrent_host_threads(env):
+    """Calls from several host threads at once, each on a stream of its own
+    (the library keeps no per-call state; the CU-count cache is atomic),
+    give the bits of the same calls made one at a time."""
+    import threading
+    torch, pg = env
+    dev = torch.device("cuda:0")
+    cases = [Workload("thr0", 0, 0, 300, 200, 500, 1.0, 0.5, seed=41),
+             Workload("thr1", 1, 1, 257, 129, 1040, -1.5, 0.0, seed=42),
+             Workload("thr2", 0, 1, 64, 96, 4096, 1.0, 1.0, seed=43, batch=3),
+             Workload("thr3", 1, 0, 640, 320, 96, 0.5, -2.0, seed=44)]
+
+    def call(w, dA, dB, dC, stream, ws):
+        # thr2 splits K across workgroups through its own workspace
+        if ws is not None:
+            return pg.sgemm_strided_batched_ws(
+                w.trans_a, w.trans_b, w.M, w.N, w.K, w.alpha, dA, w.LDA, dB, w.LDB, w.beta,
+                dC, w.LDC, w.batch, w.SA, w.SB, w.SC, ws, stream=stream, check=False)
+        return pg.sgemm_strided_batched(w.trans_a, w.trans_b, w.M, w.N, w.K, w.alpha, dA,
+                                        w.LDA, dB, w.LDB, w.beta, dC, w.LDC, w.batch, w.SA,
+                                        w.SB, w.SC, stream=stream, check=False)
+
+    def workspace(w):
+        n = pg.sgemm_workspace_size(w.trans_a, w.trans_b, w.M, w.N, w.K, w.batch)
+        return torch.empty(max(1, n // 4), device=dev) if w.name == "thr2" else None
+
+    inputs = [workloads.make_inputs(w) for w in cases]
+    want = []
+    for w, (A, B, C) in zip(cases, inputs):
+        dA, dB, dC = (torch.from_numpy(x).to(dev) for x in (A, B, C))
+        ws = workspace(w)
+        assert call(w, dA, dB, dC, torch.cuda.current_stream(dev).cuda_stream, ws) == 0
+        torch.cuda.synchronize(dev)
+        want.append(dC.cpu().numpy().view(np.uint32).copy())
+        check_against_oracle(w, A, B, C, dC.cpu().numpy())
+
+    log("[threads] 4 host threads x 25 calls")
+    errors = []
+
+    def worker(k):
+        try:
+            w, (A, B, C) = cases[k], inputs[k]
+            stream = torch.cuda.Stream(dev)
+            with torch.cuda.stream(stream):
+                dA, dB, dC0 = (torch.from_numpy(x).to(dev) for x in (A, B, C))
+                ws = workspace(w)
+                for it in range(25):
+                    dC = dC0.clone()
+                    st = call(w, dA, dB, dC, stream.cuda_stream, ws)
+                    if st != 0:
+                        errors.append((k, it, "status", st))
+                        return
+                    got = dC.cpu().numpy().view(np.uint32)  # waits for this stream
+                    if not np.array_equal(got, want[k]):
+                        errors.append((k, it, "bits differ"))
+                        return
+                stream.synchronize()
+        except Exception as e:  # reported by the main thread
+            errors.append((k, repr(e)))
+
+    threads = [threading.Thread(target=worker, args=(k,)) for k in range(len(cases))]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join(timeout=100)
+    assert not any(t.is_alive() for t in threads), "a calling thread did not finish"
+    assert not errors, errors
+
+
 def test_matmul_tensor_wrapper(env):
     torch, pg = env
     dev = torch.device("cuda:0")
