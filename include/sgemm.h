@@ -113,7 +113,10 @@ enum sgemm_variant {
                                     32-deep K-step, partial tiles added in LDS */
     SGEMM_VARIANT_M128x128_DMA = 7,/* 128 x 128 tile, 4 waves, direct-to-LDS loads into a
                                       3-stage LDS ring */
-    SGEMM_VARIANT_COUNT = 8
+    SGEMM_VARIANT_T32x64 = 8,   /*  32 x  64 tile, 8 waves (two per SIMD) each on every 8th
+                                    K-step, direct-to-LDS streaming (grids of at most one
+                                    such tile per CU) */
+    SGEMM_VARIANT_COUNT = 9
 };
 
 /*
@@ -234,8 +237,9 @@ size_t sgemm_workspace_size(int transA, int transB, int M, int N, int K, int bat
  * choice, 1 = no split, S >= 2 = slices of round_up(ceil(K / S), BK) k each
  * (BK: the variant's K-step, 16 or 32; the last slice takes the rest, so
  * fewer than S slices can result). A forced split needs its full workspace
- * (-21 otherwise) and a tile variant (-19 for SGEMM_VARIANT_T64x64, which
- * splits K across its own waves instead).
+ * (-21 otherwise) and a tile variant (-19 for the streaming variants
+ * SGEMM_VARIANT_T64x64 and SGEMM_VARIANT_T32x64, which split K across their
+ * own waves instead).
  */
 int sgemm_strided_batched_ws_variant(int transA, int transB, int M, int N, int K,
                                      float alpha, const float *A, int lda,

@@ -590,10 +590,14 @@ sgemm_mfma_kernel(Params p)
 }
 
 // ---------------------------------------------------------------------------
-// Streaming kernel for a skinny dimension over a deep K whose long operand
-// streams from HBM (never launched with split-K): a 64 x 64 tile per
-// workgroup whose WAVES waves each own every WAVES-th K-step (wave w takes
-// steps w, w+WAVES, ...) and accumulate the whole tile over their steps. Every
+// Streaming kernel for grids of few tiles over a deep K (never launched with
+// split-K): a BM x 64 tile per workgroup whose WAVES waves each own every
+// WAVES-th K-step (wave w takes steps w, w+WAVES, ...) and accumulate the
+// whole tile over their steps. Two configurations: 64 x 64 with four waves
+// and 4-deep rings, for a skinny dimension whose long operand streams from
+// HBM, and 32 x 64 with eight waves (two per SIMD) and 3-deep rings, for
+// grids of at most one such tile per CU, where a call lasts as long as one
+// workgroup's tile. Every
 // wave fills its own ring of STAGES LDS buffers with direct-to-LDS 16-byte
 // buffer loads (buffer_load_dwordx4 ... lds: lane i of an instruction writes
 // the i-th 16 bytes of a 1 KiB block, an out-of-range lane writes zeros) and
@@ -735,12 +739,12 @@ __device__ __forceinline__ void wait_vm_groups(int n)
     }
 }
 
-template <int WAVES, int STAGES, bool A_KC, bool B_KC, bool EVEN_K>
+template <int WAVES, int STAGES, int BM, int MINW, bool A_KC, bool B_KC, bool EVEN_K>
 __global__ void
-__attribute__((amdgpu_flat_work_group_size(64 * WAVES, 64 * WAVES), amdgpu_waves_per_eu(1)))
+__attribute__((amdgpu_flat_work_group_size(64 * WAVES, 64 * WAVES), amdgpu_waves_per_eu(MINW)))
 sgemm_stream_kernel(Params p)
 {
-    constexpr int BM = 64, BN = 64, BK = 16, TM = 2, TN = 2, NQ = BK / 8;
+    constexpr int BN = 64, BK = 16, TM = BM / 32, TN = 2, NQ = BK / 8;
     constexpr int RPT = BM / WAVES; // epilogue rows per thread (one column per lane)
     using OpA = DmaOperand<A_KC, BM, BK>;
     using OpB = DmaOperand<B_KC, BN, BK>;
@@ -1194,18 +1198,18 @@ constexpr VariantInfo make_dma_variant()
                           sgemm_dma_kernel<BM, BN, WM_, WN_, MW, false, true, true>}}}};
 }
 
-template <int WAVES, int STAGES>
+template <int WAVES, int STAGES, int BM, int MINW>
 constexpr VariantInfo make_stream_variant()
 {
-    return VariantInfo{64, 64, 16, 64 * WAVES, 4,
-                       {{{sgemm_stream_kernel<WAVES, STAGES, true, false, false>,
-                          sgemm_stream_kernel<WAVES, STAGES, true, false, true>},
-                         {sgemm_stream_kernel<WAVES, STAGES, true, true, false>,
-                          sgemm_stream_kernel<WAVES, STAGES, true, true, true>}},
-                        {{sgemm_stream_kernel<WAVES, STAGES, false, false, false>,
-                          sgemm_stream_kernel<WAVES, STAGES, false, false, true>},
-                         {sgemm_stream_kernel<WAVES, STAGES, false, true, false>,
-                          sgemm_stream_kernel<WAVES, STAGES, false, true, true>}}}};
+    return VariantInfo{BM, 64, 16, 64 * WAVES, 4,
+                       {{{sgemm_stream_kernel<WAVES, STAGES, BM, MINW, true, false, false>,
+                          sgemm_stream_kernel<WAVES, STAGES, BM, MINW, true, false, true>},
+                         {sgemm_stream_kernel<WAVES, STAGES, BM, MINW, true, true, false>,
+                          sgemm_stream_kernel<WAVES, STAGES, BM, MINW, true, true, true>}},
+                        {{sgemm_stream_kernel<WAVES, STAGES, BM, MINW, false, false, false>,
+                          sgemm_stream_kernel<WAVES, STAGES, BM, MINW, false, false, true>},
+                         {sgemm_stream_kernel<WAVES, STAGES, BM, MINW, false, true, false>,
+                          sgemm_stream_kernel<WAVES, STAGES, BM, MINW, false, true, true>}}}};
 }
 
 const VariantInfo kVariants[SGEMM_VARIANT_COUNT] = {
@@ -1213,13 +1217,21 @@ const VariantInfo kVariants[SGEMM_VARIANT_COUNT] = {
     make_variant<128, 128, kBK, 2, 2, 1, 2, 4>(), // SGEMM_VARIANT_M128x128
     make_variant<64, 64, kBK, 2, 2, 1, 4, 4>(),   // SGEMM_VARIANT_S64x64
     make_variant<64, 64, kBK, 2, 2, 1, 4, 1>(),   // SGEMM_VARIANT_S64x64_V1
-    make_stream_variant<4, 4>(),                  // SGEMM_VARIANT_T64x64
+    make_stream_variant<4, 4, 64, 1>(),           // SGEMM_VARIANT_T64x64
     make_variant<256, 256, kBK, 2, 4, 1, 2, 4>(), // SGEMM_VARIANT_L256x256
     make_variant<64, 64, 32, 2, 2, 2, 2, 4>(),    // SGEMM_VARIANT_S64x64_K2
     make_dma_variant<128, 128, 2, 2, 2>(),        // SGEMM_VARIANT_M128x128_DMA
+    make_stream_variant<8, 3, 32, 2>(),           // SGEMM_VARIANT_T32x64
 };
 
 long long ceil_div(long long a, long long b) { return (a + b - 1) / b; }
+
+// The streaming kernels split K across their own waves and never across
+// workgroups.
+bool is_stream(int variant)
+{
+    return variant == SGEMM_VARIANT_T64x64 || variant == SGEMM_VARIANT_T32x64;
+}
 
 int num_cus_of_current_device(int *out)
 {
@@ -1290,6 +1302,13 @@ extern "C" int sgemm_select_variant(int transA, int transB, int M, int N, int K,
         num_cus = 1;
     const long long cus = num_cus;
     const long long tiles64 = ceil_div(M, 64) * ceil_div(N, 64) * batch;
+    const long long tiles32 = ceil_div(M, 32) * ceil_div(N, 64) * batch;
+    // At most one 32 x 64 tile per CU over K >= 512: the eight-wave streaming
+    // kernel on that tile. Such a call takes as long as one workgroup's tile,
+    // and this tile is half the 64 x 64 one, with two waves per SIMD on it
+    // (8192 x 64 x 4096: 37 µs against 59 µs for the K-split 64 x 64 tile).
+    if (K >= 512 && tiles32 <= cus)
+        return SGEMM_VARIANT_T32x64;
     // One skinny dimension (<= 64) over a deep K whose long operand is too
     // large to stay in the 256 MB Infinity Cache from one call to the next
     // (over 128 MiB): the streaming kernel, whose per-wave rings keep the most
@@ -1380,7 +1399,7 @@ extern "C" int sgemm_select_splits(int transA, int transB, int M, int N, int K, 
     if (batch < 0) return -14;
     if (variant < 0 || variant >= SGEMM_VARIANT_COUNT)
         return -18;
-    if (variant == SGEMM_VARIANT_T64x64)
+    if (is_stream(variant))
         return 1;
     int kslice = 0;
     return (int)splits_for(variant, M, N, K, batch, num_cus < 1 ? 1 : num_cus, &kslice);
@@ -1460,8 +1479,8 @@ int launch(const Call &c, int variant, hipStream_t s, Split sk = Split{nullptr, 
     int splits = 1, kslice = c.K;
     if (sk.splits == 0 && sk.ws != nullptr) {
         int v = variant;
-        long long S = v == SGEMM_VARIANT_T64x64 ? 1 : splits_for(v, c.M, c.N, c.K, c.batch, cus, &kslice);
-        if (auto_variant && v == SGEMM_VARIANT_T64x64) {
+        long long S = is_stream(v) ? 1 : splits_for(v, c.M, c.N, c.K, c.batch, cus, &kslice);
+        if (auto_variant && is_stream(v)) {
             // A grid too small even for the streaming kernel's CUs: split the
             // 64 x 64 tile across workgroups instead.
             const int alt = c.K >= 768 ? SGEMM_VARIANT_S64x64_K2 : SGEMM_VARIANT_S64x64;
@@ -1489,7 +1508,7 @@ int launch(const Call &c, int variant, hipStream_t s, Split sk = Split{nullptr, 
             kslice = c.K;
         }
     } else if (sk.splits >= 2) {
-        if (variant == SGEMM_VARIANT_T64x64)
+        if (is_stream(variant))
             return -19;
         const int bk = kVariants[variant].bk;
         const long long ks = ceil_div(ceil_div(c.K, sk.splits), bk) * bk;
@@ -1696,9 +1715,9 @@ extern "C" size_t sgemm_workspace_size(int transA, int transB, int M, int N, int
     // 64 x 64 tile that replaces the streaming kernel on tiny grids.
     const int v = sgemm_select_variant(transA, transB, M, N, K, batch, 1, cus);
     int kslice = 0;
-    long long S = v == SGEMM_VARIANT_T64x64 ? 1 : splits_for(v, M, N, K, batch, cus, &kslice);
+    long long S = is_stream(v) ? 1 : splits_for(v, M, N, K, batch, cus, &kslice);
     const long long S2 = splits_for(SGEMM_VARIANT_S64x64, M, N, K, batch, cus, &kslice);
-    if (v == SGEMM_VARIANT_T64x64 && S2 > S)
+    if (is_stream(v) && S2 > S)
         S = S2;
     if (S < 2)
         return 0;

@@ -193,7 +193,12 @@ def splitk_sweep(shapes, rounds: int = 3, target_ms: float = 20.0, out=sys.stdou
         need = pg.sgemm_workspace_size(tA, tB, M, N, K, batch)
         ws = torch.empty(max(1, need // 4), device=dev)
         v = pg.sgemm_select_variant(tA, tB, M, N, K, batch, 1, cus)
-        vs = pg.VARIANT_S64x64_K2 if v == pg.VARIANT_T64x64 else v
+        # a streaming variant never splits; with a workspace the library swaps
+        # in a 64 x 64 tile when splitting that pays
+        if v in (pg.VARIANT_T64x64, pg.VARIANT_T32x64):
+            vs = pg.VARIANT_S64x64_K2 if K >= 768 else pg.VARIANT_S64x64
+        else:
+            vs = v
         splits = pg.sgemm_select_splits(tA, tB, M, N, K, batch, vs, cus) if need else 1
         calls = {
             "plain": lambda: pg.sgemm_strided_batched(tA, tB, M, N, K, 1.0, A, lda, B, ldb, 0.0,

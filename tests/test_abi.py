@@ -134,23 +134,31 @@ def test_select_variant(pg):
         assert sel(tA, 0, *shape, batch, True, 256) == pg.VARIANT_M128x128, shape
     # few 64 x 64 tiles per CU over K >= 768: the K-split eight-wave tile
     for shape in ((1024, 1024, 1024), (3072, 3072, 3072), (1536, 1536, 1536),
-                  (1024, 1024, 4096), (1000, 1000, 1000), (512, 512, 8192)):
+                  (1024, 1024, 4096), (1000, 1000, 1000)):
         assert sel(0, 0, *shape, 1, True, 256) == pg.VARIANT_S64x64_K2, shape
+    # at most one 32 x 64 tile per CU over K >= 512: the eight-wave streaming
+    # tile, skinny or not (512 x 512: 128 tiles; 1024 x 512: 256)
+    for shape in ((512, 512, 512), (512, 512, 8192), (1024, 512, 1024), (128, 128, 2048),
+                  (8192, 64, 4096), (64, 8192, 4096), (4096, 128, 4096), (64, 8192, 8192)):
+        assert sel(0, 0, *shape, 1, True, 256) == pg.VARIANT_T32x64, shape
+    assert sel(0, 0, 1024, 512, 1024, 1, True, 128) != pg.VARIANT_T32x64   # two per CU
+    assert sel(0, 0, 512, 512, 256, 1, True, 256) != pg.VARIANT_T32x64     # K < 512
     assert sel(0, 0, 512, 512, 2048, 8, True, 256) == pg.VARIANT_S64x64_K2
     # ... and the plain 64 x 64 tile below K = 768; for K <= 512 it also beats
     # the 128 x 128 tile on full grids (per-tile fixed costs dominate)
-    assert sel(0, 0, 512, 512, 512, 1, True, 256) == pg.VARIANT_S64x64
+    assert sel(0, 0, 1024, 1024, 512, 1, True, 256) == pg.VARIANT_S64x64
     assert sel(0, 0, 128, 128, 128, 1, True, 256) == pg.VARIANT_S64x64
     for shape in ((2048, 2048, 512), (4096, 4096, 256), (8192, 8192, 128), (2048, 2048, 64)):
         assert sel(0, 0, *shape, 1, True, 256) == pg.VARIANT_S64x64, shape
     assert sel(0, 0, 4096, 4096, 520, 1, True, 256) == pg.VARIANT_M128x128
-    # a skinny dimension with a long operand over 128 MiB streams, whatever
-    # the transposes; one of at most 128 MiB stays with the tiles
+    # beyond one 32 x 64 tile per CU, a skinny dimension with a long operand
+    # over 128 MiB streams through the 64 x 64 kernel, whatever the
+    # transposes; one of at most 128 MiB stays with the tiles
     for tA, tB in ((0, 1), (0, 0), (1, 1), (1, 0)):
         assert sel(tA, tB, 16384, 64, 4096, 1, True, 256) == pg.VARIANT_T64x64
-    assert sel(0, 1, 64, 8192, 8192, 1, True, 256) == pg.VARIANT_T64x64
+    assert sel(0, 1, 64, 16384, 8192, 1, True, 256) == pg.VARIANT_T64x64
     assert sel(0, 1, 16384, 64, 2048, 1, True, 256) == pg.VARIANT_S64x64_K2
-    assert sel(0, 1, 64, 8192, 4096, 1, True, 256) == pg.VARIANT_S64x64_K2
+    assert sel(0, 1, 64, 16384, 2048, 1, True, 256) == pg.VARIANT_S64x64_K2
     assert sel(0, 1, 16384, 64, 128, 1, True, 256) != pg.VARIANT_T64x64
     # the CU count enters the model: on 64 CUs 2048^3 has four 128 x 128 tiles per CU
     assert sel(0, 0, 2048, 2048, 2048, 1, True, 64) == pg.VARIANT_M128x128
@@ -219,6 +227,7 @@ def test_split_arguments_checked(pg):
     assert ws_call(pg, variant=pg.VARIANT_S64x64, splits=4, ws=(FAKE, 4 * 64 * 64 * 4 - 4),
                    **kw) == -21
     assert ws_call(pg, variant=pg.VARIANT_T64x64, splits=4, ws=(FAKE, 1 << 20), **kw) == -19
+    assert ws_call(pg, variant=pg.VARIANT_T32x64, splits=4, ws=(FAKE, 1 << 20), **kw) == -19
     for st in (-19, -20, -21):
         assert "invalid" in pg.sgemm_status_string(st) or "too small" in \
             pg.sgemm_status_string(st)
@@ -255,13 +264,16 @@ _dim = st.integers(min_value=1, max_value=1 << 16)
        batch=st.integers(1, 512), vec4=st.booleans(), cus=st.integers(1, 512))
 def test_select_variant_is_always_a_kernel(pg, tA, tB, M, N, K, batch, vec4, cus):
     """Any valid shape gets a variant in range; without 4-float loads it is the
-    1-float variant; the streaming kernel only for a dimension of at most 64."""
+    1-float variant; the 64 x 64 streaming kernel only for a dimension of at
+    most 64, the 32 x 64 one exactly for grids of at most one tile per CU."""
     v = pg.sgemm_select_variant(tA, tB, M, N, K, batch, vec4, cus)
     assert 0 <= v < pg.VARIANT_COUNT
     if not vec4:
         assert v == pg.VARIANT_S64x64_V1
     if v == pg.VARIANT_T64x64:
         assert min(M, N) <= 64 and K >= 512
+    small = K >= 512 and -(-M // 32) * -(-N // 64) * batch <= cus
+    assert (v == pg.VARIANT_T32x64) == (vec4 and small)
     assert v not in (pg.VARIANT_L256x128, pg.VARIANT_L256x256, pg.VARIANT_M128x128_DMA)
 
 
