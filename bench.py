@@ -20,8 +20,8 @@ single launches after restoring C and flushing L2 and the Infinity Cache with a
 Prints one JSON line. ``value`` is GFLOP/s (2*M*N*K per GEMM over the timed
 wall time). ``roofline`` reports the same kernel against the FP32-MFMA peak;
 ``traffic`` (HBM bytes per launch) is read from the committed rocprofv3
-counter summary if that summary was taken on the current kernel code, else
-null. ``cpu_baseline`` times the CPU oracle on a bounded sample of the same
+counter summary if that summary was taken on the current kernel code and on
+the variant this run launches, else null. ``cpu_baseline`` times the CPU oracle on a bounded sample of the same
 workload (a band of output rows) on this host's cores.
 """
 from __future__ import annotations
@@ -42,26 +42,36 @@ METRIC = "SGEMM GFLOP/s and % of FP32-MFMA peak at M=N=K=4092 (1 MI355X)"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
+HOST_SECTION = "\n// Host side\n"
+
+
 def kernel_source_hash() -> str:
-    """Hash of the kernel source's code: comments and whitespace are dropped,
-    so editing a comment keeps the counter summary current, while any change
-    to the code retires it."""
+    """Hash of the device code of the kernel source (everything before its host
+    section), comments and whitespace dropped: editing a comment or the host
+    dispatch keeps a counter summary current, while any change to a kernel
+    retires it. Which kernel a workload runs is checked separately, by variant."""
     with open(os.path.join(ROOT, "precision_gemm_amd", "csrc", "sgemm.hip")) as f:
         src = f.read()
+    cut = src.find(HOST_SECTION)
+    if cut < 0:
+        raise RuntimeError("sgemm.hip has no host section marker")
+    src = src[:cut]
     src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
     src = re.sub(r"//[^\n]*", " ", src)
     return hashlib.sha256(" ".join(src.split()).encode()).hexdigest()[:16]
 
 
-def load_traffic(workload: str):
-    """HBM bytes per launch from the committed counter summary, if current."""
+def load_traffic(workload: str, variant: str):
+    """HBM bytes per launch from the committed counter summary, if it was
+    taken on the current kernel code and on the variant this run launches."""
     try:
         with open(TRAFFIC_FILE) as f:
             data = json.load(f)
     except (OSError, ValueError):
         return None
     entry = data.get(workload)
-    if not entry or entry.get("kernel_sha") != kernel_source_hash():
+    if (not entry or entry.get("kernel_sha") != kernel_source_hash()
+            or entry.get("variant") != variant):
         return None
     return entry.get("bytes_per_launch")
 
@@ -285,7 +295,7 @@ def main(argv=None) -> int:
             "peak": peak,
             "unit": "TFLOP/s",
             "frac": round(achieved / peak, 4),
-            "traffic": load_traffic(w.name),
+            "traffic": load_traffic(w.name, pg.VARIANT_NAMES.get(variant, str(variant))),
             "arithmetic_intensity": round(roof.intensity, 2),
             "hbm_gbs_at_achieved": round(w.algorithmic_bytes() / (per_launch_ms * 1e-3) / 1e9, 1),
             "kernel_ms": round(per_launch_ms, 5),

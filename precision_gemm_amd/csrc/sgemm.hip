@@ -1303,13 +1303,12 @@ extern "C" int sgemm_select_variant(int transA, int transB, int M, int N, int K,
     const long long cus = num_cus;
     const long long tiles64 = ceil_div(M, 64) * ceil_div(N, 64) * batch;
     const long long tiles32 = ceil_div(M, 32) * ceil_div(N, 64) * batch;
-    // At most one 32 x 64 tile per CU over K >= 256: the eight-wave streaming
-    // kernel on that tile. Such a call takes as long as one workgroup's tile,
-    // and this tile is half the 64 x 64 one, with two waves per SIMD on it
-    // (8192 x 64 x 4096: 37 µs against 59 µs for the K-split 64 x 64 tile;
-    // 512 x 512 x 384: 7.0 against 8.7 µs). Below K = 256 every tile is
-    // within the cost of the call itself.
-    if (K >= 256 && tiles32 <= cus)
+    // At most one 32 x 64 tile per CU: the eight-wave streaming kernel on that
+    // tile. Such a call takes as long as one workgroup's tile, and this tile
+    // is half the 64 x 64 one, with two waves per SIMD on it (8192 x 64 x
+    // 4096: 37 µs against 59 µs for the K-split 64 x 64 tile; 512 x 512 x 384:
+    // 7.0 against 8.7 µs; 128^3: 5.3 against 6.0 µs).
+    if (tiles32 <= cus)
         return SGEMM_VARIANT_T32x64;
     // One skinny dimension (<= 64) over a deep K whose long operand is too
     // large to stay in the 256 MB Infinity Cache from one call to the next

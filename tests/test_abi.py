@@ -136,19 +136,19 @@ def test_select_variant(pg):
     for shape in ((1024, 1024, 1024), (3072, 3072, 3072), (1536, 1536, 1536),
                   (1024, 1024, 4096), (1000, 1000, 1000)):
         assert sel(0, 0, *shape, 1, True, 256) == pg.VARIANT_S64x64_K2, shape
-    # at most one 32 x 64 tile per CU over K >= 256: the eight-wave streaming
-    # tile, skinny or not (512 x 512: 128 tiles; 1024 x 512: 256)
+    # at most one 32 x 64 tile per CU: the eight-wave streaming tile, skinny
+    # or not, whatever K (512 x 512: 128 tiles; 1024 x 512: 256)
     for shape in ((512, 512, 512), (512, 512, 8192), (1024, 512, 1024), (128, 128, 2048),
-                  (512, 512, 256), (96, 96, 384),
+                  (512, 512, 256), (96, 96, 384), (128, 128, 128), (256, 256, 16),
                   (8192, 64, 4096), (64, 8192, 4096), (4096, 128, 4096), (64, 8192, 8192)):
         assert sel(0, 0, *shape, 1, True, 256) == pg.VARIANT_T32x64, shape
     assert sel(0, 0, 1024, 512, 1024, 1, True, 128) != pg.VARIANT_T32x64   # two per CU
-    assert sel(0, 0, 512, 512, 128, 1, True, 256) != pg.VARIANT_T32x64     # K < 256
+    assert sel(0, 0, 512, 512, 128, 3, True, 256) != pg.VARIANT_T32x64     # 384 tiles
     assert sel(0, 0, 512, 512, 2048, 8, True, 256) == pg.VARIANT_S64x64_K2
     # ... and the plain 64 x 64 tile below K = 768; for K <= 512 it also beats
     # the 128 x 128 tile on full grids (per-tile fixed costs dominate)
     assert sel(0, 0, 1024, 1024, 512, 1, True, 256) == pg.VARIANT_S64x64
-    assert sel(0, 0, 128, 128, 128, 1, True, 256) == pg.VARIANT_S64x64
+    assert sel(0, 0, 128, 128, 128, 1, True, 2) == pg.VARIANT_S64x64
     for shape in ((2048, 2048, 512), (4096, 4096, 256), (8192, 8192, 128), (2048, 2048, 64)):
         assert sel(0, 0, *shape, 1, True, 256) == pg.VARIANT_S64x64, shape
     assert sel(0, 0, 4096, 4096, 520, 1, True, 256) == pg.VARIANT_M128x128
@@ -273,7 +273,7 @@ def test_select_variant_is_always_a_kernel(pg, tA, tB, M, N, K, batch, vec4, cus
         assert v == pg.VARIANT_S64x64_V1
     if v == pg.VARIANT_T64x64:
         assert min(M, N) <= 64 and K >= 512
-    small = K >= 256 and -(-M // 32) * -(-N // 64) * batch <= cus
+    small = -(-M // 32) * -(-N // 64) * batch <= cus
     assert (v == pg.VARIANT_T32x64) == (vec4 and small)
     assert v not in (pg.VARIANT_L256x128, pg.VARIANT_L256x256, pg.VARIANT_M128x128_DMA)
 
