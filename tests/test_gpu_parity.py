@@ -377,6 +377,71 @@ def test_concurrent_host_threads(env):
     assert not errors, errors
 
 
+def test_graph_capture_replays(env):
+    """Calls captured into a HIP graph (the library only launches kernels on
+    the caller's stream and allocates nothing) replay to the eager bits,
+    replay after replay, with other eager work in between: a T32x64 call, a
+    K-split tile call, and a split-K call whose reduction kernel is captured
+    too (workspace allocated before the capture)."""
+    torch, pg = env
+    dev = torch.device("cuda:0")
+    cases = [Workload("g_t32", 0, 1, 256, 192, 700, 1.0, 0.5, seed=51),
+             Workload("g_k2", 1, 0, 1000, 1000, 1000, -1.0, 2.0, seed=52),
+             Workload("g_split", 0, 0, 128, 192, 8192, 0.5, 1.0, seed=53, batch=2)]
+    bufs, want = [], []
+    for w in cases:
+        A, B, C = workloads.make_inputs(w)
+        dA, dB, dC0 = (torch.from_numpy(x).to(dev) for x in (A, B, C))
+        n = pg.sgemm_workspace_size(w.trans_a, w.trans_b, w.M, w.N, w.K, w.batch)
+        ws = torch.empty(max(1, n // 4), device=dev) if w.name == "g_split" else None
+        if w.name == "g_split":
+            assert n > 0, "the split-K case must split"
+        dC = dC0.clone()
+        bufs.append((w, dA, dB, dC0, dC, ws))
+
+    def call(w, dA, dB, dC, ws):
+        if ws is not None:
+            return pg.sgemm_strided_batched_ws(
+                w.trans_a, w.trans_b, w.M, w.N, w.K, w.alpha, dA, w.LDA, dB, w.LDB, w.beta, dC,
+                w.LDC, w.batch, w.SA, w.SB, w.SC, ws)
+        return pg.sgemm_strided_batched(w.trans_a, w.trans_b, w.M, w.N, w.K, w.alpha, dA,
+                                        w.LDA, dB, w.LDB, w.beta, dC, w.LDC, w.batch, w.SA,
+                                        w.SB, w.SC)
+
+    # eager reference bits (this also fills the library's CU-count cache)
+    for w, dA, dB, dC0, dC, ws in bufs:
+        dC.copy_(dC0)
+        call(w, dA, dB, dC, ws)
+    torch.cuda.synchronize(dev)
+    want = [dC.cpu().numpy().view(np.uint32).copy() for (_, _, _, _, dC, _) in bufs]
+
+    log("[graph] capture three calls")
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream(dev)
+    side.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            for w, dA, dB, dC0, dC, ws in bufs:
+                call(w, dA, dB, dC, ws)
+    torch.cuda.current_stream(dev).wait_stream(side)
+    torch.cuda.synchronize(dev)
+
+    other = torch.rand(300, 300, device=dev)
+    for rep in range(4):
+        for w, dA, dB, dC0, dC, ws in bufs:
+            dC.copy_(dC0)  # beta != 0: every replay starts from the same C
+        torch.cuda.synchronize(dev)
+        g.replay()
+        torch.cuda.synchronize(dev)
+        for k, (w, dA, dB, dC0, dC, ws) in enumerate(bufs):
+            got = dC.cpu().numpy().view(np.uint32)
+            assert np.array_equal(got, want[k]), (rep, w.name)
+        # unrelated eager work between replays
+        pg.sgemm(0, 0, 300, 300, 300, 1.0, other, 300, other, 300, 0.0, torch.empty_like(other),
+                 300)
+        torch.cuda.synchronize(dev)
+
+
 def test_matmul_tensor_wrapper(env):
     torch, pg = env
     dev = torch.device("cuda:0")
