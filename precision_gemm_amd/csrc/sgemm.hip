@@ -1312,9 +1312,10 @@ extern "C" int sgemm_select_variant(int transA, int transB, int M, int N, int K,
         return SGEMM_VARIANT_T32x64;
     // One skinny dimension (<= 64) over a deep K whose long operand is too
     // large to stay in the 256 MB Infinity Cache from one call to the next
-    // (over 128 MiB): the streaming kernel, whose per-wave rings keep the most
-    // bytes in flight while that operand streams from HBM. A smaller long
-    // operand stays cached, and the tiles below do better on it.
+    // (over 128 MiB): the four-wave 64 x 64 streaming kernel, whose 4-deep
+    // per-wave rings keep the most bytes in flight while that operand streams
+    // from HBM. A smaller long operand stays cached, and the tiles below do
+    // better on it.
     const long long long_bytes = 4LL * (M > N ? M : N) * K * batch;
     if ((M <= 64 || N <= 64) && K >= 512 && tiles64 <= 2 * cus && long_bytes > (128LL << 20))
         return SGEMM_VARIANT_T64x64;
