@@ -238,6 +238,60 @@ def test_float_sweep_bound(env, variant):
 
 # ------------------------------------------------------------------ special cases
 
+def random_shapes(n, seed):
+    """Seeded shapes for the automatic dispatch: M, N, K log-uniform (1 to a few
+    thousand), every transpose pair, batches, padded or minimal leading
+    dimensions (which decide the 4-float path), bounded in size."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        if rng.random() < 0.4:
+            M, N = (int(np.exp(rng.uniform(0, np.log(3000)))) for _ in range(2))
+        else:
+            M, N = (int(rng.integers(200, 3000)) for _ in range(2))
+        K = int(np.exp(rng.uniform(0, np.log(6000))))
+        aligned = rng.random() < 0.75  # most real shapes are multiples of 4
+        if aligned:
+            M, N, K = (max(4, x // 4 * 4) for x in (M, N, K))
+        batch = int(rng.choice([1, 1, 1, 2, 3, 8]))
+        if M * N * batch > 4_000_000 or (M + N) * K * batch > 16_000_000:
+            continue
+        tA, tB = int(rng.integers(0, 2)), int(rng.integers(0, 2))
+        pad = (lambda: int(rng.choice([0, 0, 4, 8]))) if aligned else \
+            (lambda: int(rng.choice([0, 1, 3])))
+        a_row, b_row = (M if tA else K), (K if tB else N)
+        w = Workload(f"rnd{len(out)}", tA, tB, M, N, K, float(rng.choice([1.0, -0.5, 2.0])),
+                     float(rng.choice([0.0, 1.0, 0.25])), seed=1000 + len(out), batch=batch,
+                     lda=a_row + pad(), ldb=b_row + pad(), ldc=N + pad())
+        out.append(w)
+    return out
+
+
+def test_automatic_dispatch_random_shapes(env):
+    """120 seeded shapes through the automatic dispatch (every rule: the
+    32 x 64 streaming tile, the K-split and plain 64 x 64 tiles, the 128 x 128
+    tile, the 1-float variant), each checked against the oracle on its first
+    and last rows of every batch item, and for writes outside C's windows."""
+    torch, pg = env
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    seen = set()
+    for w in random_shapes(120, seed=77):
+        A, B, C = workloads.make_inputs(w)
+        log(f"[random] {w.name} {'NT'[w.trans_a]}{'NT'[w.trans_b]} {w.M}x{w.N}x{w.K} "
+            f"b{w.batch} ld {w.LDA},{w.LDB},{w.LDC}")
+        st, got = run_gpu(env, w, A, B, C)
+        assert st == 0, (w, st)
+        for rows in ((0, min(w.M, 6)), (max(0, w.M - 3), w.M)):
+            check_against_oracle(w, A, B, C, got, rows=rows)
+        check_untouched(w, C, got)
+        vec4 = (w.LDA % 4 == 0 and w.LDB % 4 == 0 and vec4_possible(w))
+        seen.add(pg.sgemm_select_variant(w.trans_a, w.trans_b, w.M, w.N, w.K, w.batch,
+                                         1 if vec4 else 0, cus))
+    for v in (pg.VARIANT_T32x64, pg.VARIANT_S64x64, pg.VARIANT_S64x64_K2,
+              pg.VARIANT_M128x128, pg.VARIANT_S64x64_V1):
+        assert v in seen, f"no shape reached {pg.VARIANT_NAMES[v]}"
+
+
 def test_beta_zero_ignores_nan_in_c(env):
     w = Workload("nanc", 0, 0, 130, 70, 40, 1.0, 0.0, seed=3)
     A, B, C = workloads.make_inputs(w)
