@@ -8,9 +8,11 @@
 // on-chip memory (kernel 3), register tiles reused across many products
 // (kernels 4-5, 10), 128-bit loads (kernel 6), conflict-free shared-memory
 // layouts (kernels 7-8), double buffering (its closing list) — and those of
-// "Triton Optimization Reference (cuTile -> Triton)": an EVEN_K fast path
-// with a masked tail (section 1), transposes in the load addressing (section
-// 2), a (tiles, batch) grid with grouped tile order (section 3).
+// "Triton Optimization Reference (cuTile -> Triton)": a K loop with no masks
+// and the ragged K handled apart (its EVEN_K fast path, section 1; here the
+// tile kernels move the partial K-step to the front, so one loop serves every
+// K), transposes in the load addressing (section 2), a (tiles, batch) grid
+// with grouped tile order (section 3).
 //
 // How it maps onto CDNA4:
 //   * The register tile is a grid of v_mfma_f32_32x32x2_f32 products: full
@@ -175,10 +177,12 @@ struct Operand {
     int o0;           // first outer index of this tile
     uint32_t off[NOFF];
     // Window of the next K-step to load: its first element and first k. The
-    // buffer range of a window is the bytes left from its start to the end of
-    // the operand, capped at 2^31 - 1: while `big` is positive the window is
-    // capped, after that `rem` holds the exact bytes left (negative once past
-    // the end). Both advance with 32-bit scalar arithmetic only.
+    // first window starts at k = kfirst <= 0, so that a K that is not a
+    // multiple of BK leaves its partial step first and every later step full.
+    // The buffer range of a window is the bytes left from its start to the
+    // end of the operand, capped at 2^31 - 1: while `big` is positive the
+    // window is capped, after that `rem` holds the exact bytes left (negative
+    // once past the end). Both advance with 32-bit scalar arithmetic only.
     const float *wp;
     int kn;
     int32_t big;
@@ -193,7 +197,7 @@ struct Operand {
         return KC ? r * BK + 4 * (c4 ^ swz(r)) : r * ROW + 4 * c4;
     }
 
-    __device__ __forceinline__ void init(int tid)
+    __device__ __forceinline__ void init(int tid, int kfirst)
     {
 #pragma unroll
         for (int s = 0; s < SLOTS; ++s) {
@@ -207,9 +211,12 @@ struct Operand {
                 off[s * EPS + e] = ok ? (uint32_t)((elem + e) * 4) : kOOB;
             }
         }
-        const long long base = KC ? (long long)o0 * ld : (long long)o0;
-        wp = X + base;
-        kn = 0;
+        // (kfirst < 0 moves the first window before the tile's k = 0; the
+        // lanes there are masked, and the address is formed as an integer.)
+        const long long base = (KC ? (long long)o0 * ld : (long long)o0) +
+                               (KC ? (long long)kfirst : (long long)kfirst * ld);
+        wp = reinterpret_cast<const float *>(reinterpret_cast<uintptr_t>(X) + 4 * base);
+        kn = kfirst;
         step_bytes = (int32_t)(KC ? 4LL * BK : 4LL * BK * ld);
         const long long left = 4 * (total - base);
         if (left > (long long)kMaxRange) {
@@ -223,7 +230,7 @@ struct Operand {
     }
 
     // Issue the loads of the next K-step into regs and advance the window.
-    // TAIL: also mask k >= K (needed only for a partial last step).
+    // TAIL: also mask k outside [0, K) (needed only for the partial first step).
     template <bool TAIL>
     __device__ __forceinline__ void load_next(int tid, f32x4 (&regs)[SLOTS])
     {
@@ -236,7 +243,7 @@ struct Operand {
             const int f = tid + s * NT, r = f / C4, c4 = f % C4;
             if (VEC == 4) {
                 uint32_t o = off[s];
-                if (TAIL && !(KC ? (kn + 4 * c4 < K) : (kn + r < K)))
+                if (TAIL && !((uint32_t)(KC ? kn + 4 * c4 : kn + r) < (uint32_t)K))
                     o |= kOOB;
                 regs[s] = load4(rs, o);
             } else {
@@ -244,7 +251,7 @@ struct Operand {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     uint32_t o = off[s * 4 + e];
-                    if (TAIL && !(KC ? (kn + 4 * c4 + e < K) : (kn + r < K)))
+                    if (TAIL && !((uint32_t)(KC ? kn + 4 * c4 + e : kn + r) < (uint32_t)K))
                         o |= kOOB;
                     v[e] = load1(rs, o);
                 }
@@ -362,7 +369,7 @@ __device__ __forceinline__ void store_tile(const Params &p, float *Cb, int m0, i
 // the end in a fixed order (group 0's plus group 1's), so results do not
 // depend on timing.
 template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int WAVES_K, int MIN_WAVES_PER_EU,
-          bool A_KC, bool B_KC, bool EVEN_K, int VEC>
+          bool A_KC, bool B_KC, int VEC>
 __global__ void
 __attribute__((amdgpu_flat_work_group_size(64 * WAVES_M * WAVES_N * WAVES_K,
                                            64 * WAVES_M * WAVES_N * WAVES_K),
@@ -413,7 +420,9 @@ sgemm_mfma_kernel(Params p)
     opa.O = p.M;
     opa.K = Kt;
     opa.o0 = m0;
-    opa.init(tid);
+    // A K that is not a multiple of BK puts its partial step first.
+    const int kfirst = Kt % BK == 0 ? 0 : Kt % BK - BK;
+    opa.init(tid, kfirst);
     OpB opb;
     opb.X = Bb;
     opb.ld = p.ldb;
@@ -421,7 +430,7 @@ sgemm_mfma_kernel(Params p)
     opb.O = p.N;
     opb.K = Kt;
     opb.o0 = n0;
-    opb.init(tid);
+    opb.init(tid, kfirst);
 
     f32x16 acc[TM][TN];
 #pragma unroll
@@ -433,10 +442,12 @@ sgemm_mfma_kernel(Params p)
     f32x4 ra[OpA::SLOTS], rb[OpB::SLOTS];
     const int nsteps = (Kt + BK - 1) / BK;
 
-    // EVEN_K: every K-step is full and no load carries a k mask. Otherwise
-    // only the copies of the loop body that can load the partial last step
-    // (the prologue and the last iterations) compare k against K.
-    using Tail = std::bool_constant<!EVEN_K>;
+    // Every K-step after the first is full, so only the prologue's first load
+    // carries a k mask (a no-op when K is a multiple of BK): the K loop is the
+    // same code for every K. (With a partial last step instead, the masked
+    // copy of the kernel compiled to a schedule 24 % slower for two
+    // k-contiguous operands.)
+    using Masked = std::true_type;
     using Full = std::false_type;
     auto load = [&](auto tail) {
         opa.template load_next<decltype(tail)::value>(tid, ra);
@@ -469,10 +480,10 @@ sgemm_mfma_kernel(Params p)
         }
     };
 
-    load(Tail{});
+    load(Masked{});
     OpA::store(lds, tid, ra);
     OpB::store(lds + OpA::STAGE, tid, rb);
-    load(Tail{});
+    load(Full{});
     __syncthreads();
 
     // Software pipeline over K-steps. Group 0 of a stage is read right after
@@ -527,20 +538,16 @@ sgemm_mfma_kernel(Params p)
     };
     using P0 = std::integral_constant<int, 0>;
     using P1 = std::integral_constant<int, 1>;
-    // Step s loads step s + 2; only a load of the partial last step needs the
-    // k mask, so steps before nsteps - 3 run unmasked, two per trip.
-    const int unmasked = EVEN_K ? nsteps : nsteps - 3;
+    // Step s loads step s + 2 (the loads of the last two steps read nothing
+    // that is used), two steps per trip.
     int s = 0;
-    for (; s + 1 < unmasked; s += 2) {
+    for (; s + 1 < nsteps; s += 2) {
         k_step(P0{}, Full{});
         k_step(P1{}, Full{});
     }
-    // The pairs above end on an even step, so the rest starts at parity 0.
-    for (; s < nsteps; s += 2) {
-        k_step(P0{}, Tail{});
-        if (s + 1 < nsteps)
-            k_step(P1{}, Tail{});
-    }
+    // An odd last step (the pairs above end on an even step: parity 0).
+    if (s < nsteps)
+        k_step(P0{}, Full{});
 
     // Accumulator register v of lane l holds row 8*(v/4) + 4*(l/32) + v%4,
     // column l%32 of its 32 x 32 product. With WAVES_K = 2, wave group h
@@ -1169,19 +1176,21 @@ struct VariantInfo {
 
 constexpr int kBK = 16;
 
+// The tile kernels take any K with one K loop (a partial step goes first), so
+// both even_k entries of a transpose pair name the same kernel.
 template <int BM, int BN, int BK, int WM_, int WN_, int WK_, int MW, int VEC>
 constexpr VariantInfo make_variant()
 {
     return VariantInfo{
         BM, BN, BK, 64 * WM_ * WN_ * WK_, VEC,
-        {{{sgemm_mfma_kernel<BM, BN, BK, WM_, WN_, WK_, MW, true, false, false, VEC>,
-           sgemm_mfma_kernel<BM, BN, BK, WM_, WN_, WK_, MW, true, false, true, VEC>},
-          {sgemm_mfma_kernel<BM, BN, BK, WM_, WN_, WK_, MW, true, true, false, VEC>,
-           sgemm_mfma_kernel<BM, BN, BK, WM_, WN_, WK_, MW, true, true, true, VEC>}},
-         {{sgemm_mfma_kernel<BM, BN, BK, WM_, WN_, WK_, MW, false, false, false, VEC>,
-           sgemm_mfma_kernel<BM, BN, BK, WM_, WN_, WK_, MW, false, false, true, VEC>},
-          {sgemm_mfma_kernel<BM, BN, BK, WM_, WN_, WK_, MW, false, true, false, VEC>,
-           sgemm_mfma_kernel<BM, BN, BK, WM_, WN_, WK_, MW, false, true, true, VEC>}}}};
+        {{{sgemm_mfma_kernel<BM, BN, BK, WM_, WN_, WK_, MW, true, false, VEC>,
+           sgemm_mfma_kernel<BM, BN, BK, WM_, WN_, WK_, MW, true, false, VEC>},
+          {sgemm_mfma_kernel<BM, BN, BK, WM_, WN_, WK_, MW, true, true, VEC>,
+           sgemm_mfma_kernel<BM, BN, BK, WM_, WN_, WK_, MW, true, true, VEC>}},
+         {{sgemm_mfma_kernel<BM, BN, BK, WM_, WN_, WK_, MW, false, false, VEC>,
+           sgemm_mfma_kernel<BM, BN, BK, WM_, WN_, WK_, MW, false, false, VEC>},
+          {sgemm_mfma_kernel<BM, BN, BK, WM_, WN_, WK_, MW, false, true, VEC>,
+           sgemm_mfma_kernel<BM, BN, BK, WM_, WN_, WK_, MW, false, true, VEC>}}}};
 }
 
 template <int BM, int BN, int WM_, int WN_, int MW>
