@@ -73,3 +73,48 @@ def test_mfma_issue_rate(probes):
     sys.stdout.flush()
     # a sanity floor only: the rate depends on the clock the device runs at
     assert tf.value > 0.5 * 157.3 * cus / 256
+
+
+def test_no_schedule_cliff_across_transposes():
+    """The 128 x 128 tile runs the same work at about the same speed for every
+    transpose pair and for K with or without a partial K-step (4096^2 x K).
+    A kernel whose compiled schedule falls off a cliff for one of them (an
+    earlier build ran NT with K = 4092 24 % slower) fails this; the margin,
+    12 % over the median, is far above run-to-run noise."""
+    import statistics
+    import time
+
+    import torch
+
+    import precision_gemm_amd as pg
+    dev = torch.device("cuda:0")
+    s = torch.cuda.current_stream(dev)
+    n = 4096
+    A, B, C = (torch.rand(n * n, device=dev) for _ in range(3))
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < 0.3:  # clock ramp
+        pg.sgemm(0, 0, n, n, n, 1.0, A, n, B, n, 0.0, C, n)
+        torch.cuda.synchronize(dev)
+
+    def timed(tA, tB, K):
+        def call():
+            pg.sgemm_strided_batched_variant(tA, tB, n, n, K, 1.0, A, n, B, n, 0.0, C, n, 1, 0, 0,
+                                             0, pg.VARIANT_M128x128)
+        for _ in range(3):
+            call()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(s)
+        for _ in range(8):
+            call()
+        e1.record(s)
+        e1.synchronize()
+        return e0.elapsed_time(e1) / 8
+
+    cases = [(tA, tB, K) for tA in (0, 1) for tB in (0, 1) for K in (4096, 4092)]
+    times = {c: statistics.median(timed(*c) for _ in range(3)) for c in cases}
+    med = statistics.median(times.values())
+    sys.stdout.write("transpose/K times (ms): " +
+                     ", ".join(f"{'NT'[a]}{'NT'[b]} K{k}={t:.3f}" for (a, b, k), t in times.items())
+                     + "\n")
+    slow = {c: t for c, t in times.items() if t > 1.12 * med}
+    assert not slow, f"schedule cliff: {slow} against a median of {med:.3f} ms"
