@@ -662,8 +662,10 @@ struct DmaOperand {
             const bool ok = KC ? (o0 + r < O) : (o0 + 4 * c < O);
             off[i] = ok ? (uint32_t)(((long long)r * ld + 4 * c) * 4) : kOOB;
         }
+        // (k0 < 0: the window starts before the tile's k = 0; those lanes are
+        // masked, and the address is formed as an integer.)
         const long long base = KC ? (long long)o0 * ld + k0 : (long long)k0 * ld + o0;
-        wp = X + base;
+        wp = reinterpret_cast<const float *>(reinterpret_cast<uintptr_t>(X) + 4 * base);
         kn = k0;
         kstep = kstride;
         step_elems = KC ? (long long)kstride : (long long)kstride * ld;
@@ -694,7 +696,7 @@ struct DmaOperand {
             if (TAIL) {
                 int r, c;
                 chunk(b, lane, r, c);
-                if (!(KC ? (kn + 4 * c < K) : (kn + r < K)))
+                if (!((uint32_t)(KC ? kn + 4 * c : kn + r) < (uint32_t)K))
                     o |= kOOB;
             }
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
@@ -746,7 +748,7 @@ __device__ __forceinline__ void wait_vm_groups(int n)
     }
 }
 
-template <int WAVES, int STAGES, int BM, int MINW, bool A_KC, bool B_KC, bool EVEN_K>
+template <int WAVES, int STAGES, int BM, int MINW, bool A_KC, bool B_KC>
 __global__ void
 __attribute__((amdgpu_flat_work_group_size(64 * WAVES, 64 * WAVES), amdgpu_waves_per_eu(MINW)))
 sgemm_stream_kernel(Params p)
@@ -786,7 +788,10 @@ sgemm_stream_kernel(Params p)
     opa.O = p.M;
     opa.K = p.K;
     opa.o0 = m0;
-    opa.init(lane, wave * BK, WAVES * BK);
+    // A K that is not a multiple of BK puts its partial step first (wave 0's
+    // first step): only the first load of each wave carries a k mask.
+    const int kfirst = p.K % BK == 0 ? 0 : p.K % BK - BK;
+    opa.init(lane, kfirst + wave * BK, WAVES * BK);
     OpB opb;
     opb.X = Bb;
     opb.ld = p.ldb;
@@ -794,14 +799,14 @@ sgemm_stream_kernel(Params p)
     opb.O = p.N;
     opb.K = p.K;
     opb.o0 = n0;
-    opb.init(lane, wave * BK, WAVES * BK);
+    opb.init(lane, kfirst + wave * BK, WAVES * BK);
 
     float *ring = lds + wave * STAGES * STAGE;
     // My j-th step is K-step wave + WAVES j; its loads go to ring slot j % STAGES.
-    auto issue = [&](int j) {
+    auto issue = [&](int j, auto masked) {
         float *slot = ring + (j % STAGES) * STAGE;
-        opa.template issue<!EVEN_K>(slot, lane);
-        opb.template issue<!EVEN_K>(slot + OpA::FLOATS, lane);
+        opa.template issue<decltype(masked)::value>(slot, lane);
+        opb.template issue<decltype(masked)::value>(slot + OpA::FLOATS, lane);
     };
     float fa[2][NQ][TM][4], fb[2][NQ][TN][4];
     auto read = [&](int j, float (&xa)[NQ][TM][4], float (&xb)[NQ][TN][4]) {
@@ -829,10 +834,12 @@ sgemm_stream_kernel(Params p)
     // it in flight (vector-memory operations complete in issue order).
     const int nsteps = (p.K + BK - 1) / BK;
     const int mine = wave < nsteps ? (nsteps - wave + WAVES - 1) / WAVES : 0;
+    if (mine > 0)
+        issue(0, std::true_type{});
 #pragma unroll
-    for (int j = 0; j < STAGES - 1; ++j)
+    for (int j = 1; j < STAGES - 1; ++j)
         if (j < mine)
-            issue(j);
+            issue(j, std::false_type{});
     wait_vm_groups<NI, STAGES - 2>(mine - 1);
     read(0, fa[0], fb[0]);
     // Step i: issue step i + STAGES - 1 (if it exists), wait for step i + 1,
@@ -841,10 +848,10 @@ sgemm_stream_kernel(Params p)
     auto step = [&](auto h, auto steady, int i) {
         constexpr int H = decltype(h)::value;
         if (decltype(steady)::value) {
-            issue(i + STAGES - 1);
+            issue(i + STAGES - 1, std::false_type{});
             __builtin_amdgcn_s_waitcnt(waitcnt_vm((STAGES - 2) * NI));
         } else if (i + STAGES - 1 < mine) {
-            issue(i + STAGES - 1);
+            issue(i + STAGES - 1, std::false_type{});
             __builtin_amdgcn_s_waitcnt(waitcnt_vm((STAGES - 2) * NI));
         } else {
             wait_vm_groups<NI, STAGES - 2>(mine - 2 - i); // steps issued after i + 1
@@ -1207,18 +1214,19 @@ constexpr VariantInfo make_dma_variant()
                           sgemm_dma_kernel<BM, BN, WM_, WN_, MW, false, true, true>}}}};
 }
 
+// The streaming kernels, like the tile kernels, take any K with one K loop.
 template <int WAVES, int STAGES, int BM, int MINW>
 constexpr VariantInfo make_stream_variant()
 {
     return VariantInfo{BM, 64, 16, 64 * WAVES, 4,
-                       {{{sgemm_stream_kernel<WAVES, STAGES, BM, MINW, true, false, false>,
-                          sgemm_stream_kernel<WAVES, STAGES, BM, MINW, true, false, true>},
-                         {sgemm_stream_kernel<WAVES, STAGES, BM, MINW, true, true, false>,
-                          sgemm_stream_kernel<WAVES, STAGES, BM, MINW, true, true, true>}},
-                        {{sgemm_stream_kernel<WAVES, STAGES, BM, MINW, false, false, false>,
-                          sgemm_stream_kernel<WAVES, STAGES, BM, MINW, false, false, true>},
-                         {sgemm_stream_kernel<WAVES, STAGES, BM, MINW, false, true, false>,
-                          sgemm_stream_kernel<WAVES, STAGES, BM, MINW, false, true, true>}}}};
+                       {{{sgemm_stream_kernel<WAVES, STAGES, BM, MINW, true, false>,
+                          sgemm_stream_kernel<WAVES, STAGES, BM, MINW, true, false>},
+                         {sgemm_stream_kernel<WAVES, STAGES, BM, MINW, true, true>,
+                          sgemm_stream_kernel<WAVES, STAGES, BM, MINW, true, true>}},
+                        {{sgemm_stream_kernel<WAVES, STAGES, BM, MINW, false, false>,
+                          sgemm_stream_kernel<WAVES, STAGES, BM, MINW, false, false>},
+                         {sgemm_stream_kernel<WAVES, STAGES, BM, MINW, false, true>,
+                          sgemm_stream_kernel<WAVES, STAGES, BM, MINW, false, true>}}}};
 }
 
 const VariantInfo kVariants[SGEMM_VARIANT_COUNT] = {
