@@ -946,8 +946,7 @@ sgemm_stream_kernel(Params p)
 // issue order), and the barrier then publishes step s+1 to all waves. The
 // loads stop at the last step, so none is pending when the workgroup ends.
 // ---------------------------------------------------------------------------
-template <int BM, int BN, int WAVES_M, int WAVES_N, int MIN_WAVES_PER_EU, bool A_KC, bool B_KC,
-          bool EVEN_K>
+template <int BM, int BN, int WAVES_M, int WAVES_N, int MIN_WAVES_PER_EU, bool A_KC, bool B_KC>
 __global__ void
 __attribute__((amdgpu_flat_work_group_size(64 * WAVES_M * WAVES_N, 64 * WAVES_M * WAVES_N),
                amdgpu_waves_per_eu(MIN_WAVES_PER_EU)))
@@ -995,7 +994,10 @@ sgemm_dma_kernel(Params p)
     da.O = p.M;
     da.K = Kt;
     da.o0 = m0;
-    da.init(lane, 0, BK, wave);
+    // A K that is not a multiple of BK puts its partial step first, as in
+    // sgemm_mfma_kernel: only the first step's loads carry a k mask.
+    const int kfirst = Kt % BK == 0 ? 0 : Kt % BK - BK;
+    da.init(lane, kfirst, BK, wave);
     DB db;
     db.X = Bb;
     db.ld = p.ldb;
@@ -1003,7 +1005,7 @@ sgemm_dma_kernel(Params p)
     db.O = p.N;
     db.K = Kt;
     db.o0 = n0;
-    db.init(lane, 0, BK, wave);
+    db.init(lane, kfirst, BK, wave);
 
     f32x16 acc[TM][TN];
 #pragma unroll
@@ -1037,10 +1039,9 @@ sgemm_dma_kernel(Params p)
     };
 
     // Steps 0 and 1 into stages 0 and 1; wait for step 0.
-    using Tail = std::bool_constant<!EVEN_K>;
-    issue(lds, Tail{});
+    issue(lds, std::true_type{});
     if (nsteps > 1) {
-        issue(lds + STAGE, Tail{});
+        issue(lds + STAGE, std::false_type{});
         __builtin_amdgcn_s_waitcnt(waitcnt_vm(NI));
     } else {
         __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
@@ -1049,9 +1050,9 @@ sgemm_dma_kernel(Params p)
     float fa[NQ][TM][4], fb[NQ][TN][4];
     read_group(lds, 0, fa[0], fb[0]);
 
-    // Step s in stage STG = s % 3. MODE 0 issues step s+2 without the k mask,
-    // 1 with it (it may be the partial last step), 2 issues nothing (s+2 is
-    // past the last step).
+    // Step s in stage STG = s % 3. MODE 0 issues step s+2 (every step after
+    // the first is full, so without a k mask), 2 issues nothing (s+2 is past
+    // the last step).
     auto k_step = [&](auto stg, auto mode) {
         constexpr int STG = decltype(stg)::value, MODE = decltype(mode)::value;
         const float *cur = lds + STG * STAGE;
@@ -1059,8 +1060,6 @@ sgemm_dma_kernel(Params p)
         float *ahead = lds + ((STG + 2) % 3) * STAGE;
         if constexpr (MODE == 0)
             issue(ahead, std::false_type{});
-        else if constexpr (MODE == 1)
-            issue(ahead, std::true_type{});
 #pragma unroll
         for (int q = 1; q < NQ; ++q)
             read_group(cur, q, fa[q], fb[q]);
@@ -1091,11 +1090,9 @@ sgemm_dma_kernel(Params p)
     using S1 = std::integral_constant<int, 1>;
     using S2 = std::integral_constant<int, 2>;
     using Plain = std::integral_constant<int, 0>;
-    using Masked = std::integral_constant<int, 1>;
     using NoLoad = std::integral_constant<int, 2>;
-    // Steps before `steady` issue unmasked loads: all with s + 2 < nsteps if
-    // K is a multiple of BK, else all but the one issuing the last step.
-    const int steady = EVEN_K ? nsteps - 2 : nsteps - 3;
+    // Steps before `steady` (those with s + 2 < nsteps) issue the loads of step s + 2.
+    const int steady = nsteps - 2;
     int s = 0;
     for (; s + 3 <= steady; s += 3) {
         k_step(S0{}, Plain{});
@@ -1106,8 +1103,6 @@ sgemm_dma_kernel(Params p)
     auto any_step = [&](auto stg, int st) {
         if (st < steady)
             k_step(stg, Plain{});
-        else if (st + 2 < nsteps)
-            k_step(stg, Masked{});
         else
             k_step(stg, NoLoad{});
     };
@@ -1178,55 +1173,39 @@ typedef void (*KernelFn)(Params);
 
 struct VariantInfo {
     int bm, bn, bk, threads, vec;
-    KernelFn fn[2][2][2]; // [transA][transB][even_k]
+    KernelFn fn[2][2]; // [transA][transB]; every kernel takes any K
 };
 
 constexpr int kBK = 16;
 
-// The tile kernels take any K with one K loop (a partial step goes first), so
-// both even_k entries of a transpose pair name the same kernel.
 template <int BM, int BN, int BK, int WM_, int WN_, int WK_, int MW, int VEC>
 constexpr VariantInfo make_variant()
 {
-    return VariantInfo{
-        BM, BN, BK, 64 * WM_ * WN_ * WK_, VEC,
-        {{{sgemm_mfma_kernel<BM, BN, BK, WM_, WN_, WK_, MW, true, false, VEC>,
-           sgemm_mfma_kernel<BM, BN, BK, WM_, WN_, WK_, MW, true, false, VEC>},
-          {sgemm_mfma_kernel<BM, BN, BK, WM_, WN_, WK_, MW, true, true, VEC>,
-           sgemm_mfma_kernel<BM, BN, BK, WM_, WN_, WK_, MW, true, true, VEC>}},
-         {{sgemm_mfma_kernel<BM, BN, BK, WM_, WN_, WK_, MW, false, false, VEC>,
-           sgemm_mfma_kernel<BM, BN, BK, WM_, WN_, WK_, MW, false, false, VEC>},
-          {sgemm_mfma_kernel<BM, BN, BK, WM_, WN_, WK_, MW, false, true, VEC>,
-           sgemm_mfma_kernel<BM, BN, BK, WM_, WN_, WK_, MW, false, true, VEC>}}}};
+    return VariantInfo{BM, BN, BK, 64 * WM_ * WN_ * WK_, VEC,
+                       {{sgemm_mfma_kernel<BM, BN, BK, WM_, WN_, WK_, MW, true, false, VEC>,
+                         sgemm_mfma_kernel<BM, BN, BK, WM_, WN_, WK_, MW, true, true, VEC>},
+                        {sgemm_mfma_kernel<BM, BN, BK, WM_, WN_, WK_, MW, false, false, VEC>,
+                         sgemm_mfma_kernel<BM, BN, BK, WM_, WN_, WK_, MW, false, true, VEC>}}};
 }
 
 template <int BM, int BN, int WM_, int WN_, int MW>
 constexpr VariantInfo make_dma_variant()
 {
     return VariantInfo{BM, BN, 16, 64 * WM_ * WN_, 4,
-                       {{{sgemm_dma_kernel<BM, BN, WM_, WN_, MW, true, false, false>,
-                          sgemm_dma_kernel<BM, BN, WM_, WN_, MW, true, false, true>},
-                         {sgemm_dma_kernel<BM, BN, WM_, WN_, MW, true, true, false>,
-                          sgemm_dma_kernel<BM, BN, WM_, WN_, MW, true, true, true>}},
-                        {{sgemm_dma_kernel<BM, BN, WM_, WN_, MW, false, false, false>,
-                          sgemm_dma_kernel<BM, BN, WM_, WN_, MW, false, false, true>},
-                         {sgemm_dma_kernel<BM, BN, WM_, WN_, MW, false, true, false>,
-                          sgemm_dma_kernel<BM, BN, WM_, WN_, MW, false, true, true>}}}};
+                       {{sgemm_dma_kernel<BM, BN, WM_, WN_, MW, true, false>,
+                         sgemm_dma_kernel<BM, BN, WM_, WN_, MW, true, true>},
+                        {sgemm_dma_kernel<BM, BN, WM_, WN_, MW, false, false>,
+                         sgemm_dma_kernel<BM, BN, WM_, WN_, MW, false, true>}}};
 }
 
-// The streaming kernels, like the tile kernels, take any K with one K loop.
 template <int WAVES, int STAGES, int BM, int MINW>
 constexpr VariantInfo make_stream_variant()
 {
     return VariantInfo{BM, 64, 16, 64 * WAVES, 4,
-                       {{{sgemm_stream_kernel<WAVES, STAGES, BM, MINW, true, false>,
-                          sgemm_stream_kernel<WAVES, STAGES, BM, MINW, true, false>},
-                         {sgemm_stream_kernel<WAVES, STAGES, BM, MINW, true, true>,
-                          sgemm_stream_kernel<WAVES, STAGES, BM, MINW, true, true>}},
-                        {{sgemm_stream_kernel<WAVES, STAGES, BM, MINW, false, false>,
-                          sgemm_stream_kernel<WAVES, STAGES, BM, MINW, false, false>},
-                         {sgemm_stream_kernel<WAVES, STAGES, BM, MINW, false, true>,
-                          sgemm_stream_kernel<WAVES, STAGES, BM, MINW, false, true>}}}};
+                       {{sgemm_stream_kernel<WAVES, STAGES, BM, MINW, true, false>,
+                         sgemm_stream_kernel<WAVES, STAGES, BM, MINW, true, true>},
+                        {sgemm_stream_kernel<WAVES, STAGES, BM, MINW, false, false>,
+                         sgemm_stream_kernel<WAVES, STAGES, BM, MINW, false, true>}}};
 }
 
 const VariantInfo kVariants[SGEMM_VARIANT_COUNT] = {
@@ -1547,7 +1526,6 @@ int launch(const Call &c, int variant, hipStream_t s, Split sk = Split{nullptr, 
     const long long tiles_item = ceil_div(c.M, vi.bm) * ceil_div(c.N, vi.bn);
     if (tiles_item * vi.threads > INT32_MAX || (long long)splits * tiles_item > INT32_MAX)
         return -22;
-    const int even_k = c.K % vi.bk == 0 ? 1 : 0;
     Params p;
     p.A = c.A;
     p.B = c.B;
@@ -1589,7 +1567,7 @@ int launch(const Call &c, int variant, hipStream_t s, Split sk = Split{nullptr, 
     if (max_flat > 65535)
         max_flat = 65535;
     max_flat -= max_flat % splits; // >= splits: splits * per_batch <= INT32_MAX above
-    KernelFn fn = vi.fn[c.tA][c.tB][even_k];
+    KernelFn fn = vi.fn[c.tA][c.tB];
     for (long long b0 = 0; b0 < flat; b0 += max_flat) {
         const long long nb = flat - b0 < max_flat ? flat - b0 : max_flat;
         const long long i0 = b0 / splits; // first batch item of this launch
