@@ -504,8 +504,9 @@ sgemm_mfma_kernel(Params p)
             read_group(cur, q, fa[q], fb[q]);
         mfma_group(fa[0], fb[0], 0, 4 * TM * TN);
         // The stage written here is idle this step. On the last two steps the
-        // writes and loads are of no use but harmless (loads past the operand
-        // read zero through the buffer range).
+        // writes and loads are of no use but harmless (their windows lie past
+        // the last K-step; a lane reads either memory inside the operand's
+        // buffer range or, beyond it, zeros).
         OpA::store(nxt, tid, ra);
         OpB::store(nxt + OpA::STAGE, tid, rb);
         load(tail);
@@ -682,6 +683,8 @@ struct DmaOperand {
     }
 
     // Load this wave's next K-step into `tile` and advance the window.
+    // TAIL: also mask k outside [0, K) (needed only for a first window that
+    // starts before k = 0).
     template <bool TAIL>
     __device__ __forceinline__ void issue(float *tile, int lane)
     {
