@@ -115,8 +115,11 @@ enum sgemm_variant {
                                       3-stage LDS ring */
     SGEMM_VARIANT_T32x64 = 8,   /*  32 x  64 tile, 8 waves (two per SIMD) each on every 8th
                                     K-step, direct-to-LDS streaming (grids of at most one
-                                    such tile per CU) */
-    SGEMM_VARIANT_COUNT = 9
+                                    such tile per CU over K < 512, or M <= 32) */
+    SGEMM_VARIANT_T64x32 = 9,   /*  64 x  32 tile, the same kernel (grids of at most one
+                                    such tile per CU over K >= 512, N <= 32, or a last
+                                    round of tiles it fills better) */
+    SGEMM_VARIANT_COUNT = 10
 };
 
 /*
@@ -238,8 +241,8 @@ size_t sgemm_workspace_size(int transA, int transB, int M, int N, int K, int bat
  * (BK: the variant's K-step, 16 or 32; the last slice takes the rest, so
  * fewer than S slices can result). A forced split needs its full workspace
  * (-21 otherwise) and a tile variant (-19 for the streaming variants
- * SGEMM_VARIANT_T64x64 and SGEMM_VARIANT_T32x64, which split K across their
- * own waves instead).
+ * SGEMM_VARIANT_T64x64, SGEMM_VARIANT_T32x64 and SGEMM_VARIANT_T64x32, which
+ * split K across their own waves instead).
  */
 int sgemm_strided_batched_ws_variant(int transA, int transB, int M, int N, int K,
                                      float alpha, const float *A, int lda,

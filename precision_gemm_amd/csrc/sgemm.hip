@@ -751,13 +751,15 @@ __device__ __forceinline__ void wait_vm_groups(int n)
     }
 }
 
-template <int WAVES, int STAGES, int BM, int MINW, bool A_KC, bool B_KC>
+template <int WAVES, int STAGES, int BM, int BN, int MINW, bool A_KC, bool B_KC>
 __global__ void
 __attribute__((amdgpu_flat_work_group_size(64 * WAVES, 64 * WAVES), amdgpu_waves_per_eu(MINW)))
 sgemm_stream_kernel(Params p)
 {
-    constexpr int BN = 64, BK = 16, TM = BM / 32, TN = 2, NQ = BK / 8;
-    constexpr int RPT = BM / WAVES; // epilogue rows per thread (one column per lane)
+    constexpr int BK = 16, TM = BM / 32, TN = BN / 32, NQ = BK / 8;
+    // Epilogue: a wave covers 64 / BN rows per pass (one column per lane).
+    constexpr int RPW = 64 / BN;
+    constexpr int RPT = BM / (WAVES * RPW); // epilogue rows per thread
     using OpA = DmaOperand<A_KC, BM, BK>;
     using OpB = DmaOperand<B_KC, BN, BK>;
     constexpr int STAGE = OpA::FLOATS + OpB::FLOATS;      // floats per ring slot
@@ -766,7 +768,7 @@ sgemm_stream_kernel(Params p)
     constexpr int RING = WAVES * STAGES * STAGE;
     constexpr int PART = WAVES * BM * PITCH;
     static_assert((STAGES - 2) * NI <= 63 && RPT <= 63, "vmcnt holds at most 63");
-    static_assert(BN == 64 && BM % WAVES == 0, "epilogue split");
+    static_assert((BN == 64 || BN == 32) && BM % (WAVES * RPW) == 0, "epilogue split");
     __shared__ __attribute__((aligned(16))) float lds[RING > PART ? RING : PART];
 
     int b, tile_m, tile_n;
@@ -903,18 +905,20 @@ sgemm_stream_kernel(Params p)
                 part[(32 * i + 8 * (v >> 2) + 4 * g + (v & 3)) * PITCH + 32 * t + (lane & 31)] =
                     acc[i][t][v];
 
-    // Epilogue: thread (wave, lane) finishes column `lane` of rows wave + WAVES*r,
-    // so every C access of a wave is one contiguous row. With beta != 0 the C
-    // loads are issued before the barrier and land while the partials are summed.
+    // Epilogue: thread (wave, lane) finishes column lane % BN of rows
+    // RPW * (wave + WAVES * r) + lane / BN, so every C access of a wave covers
+    // whole contiguous row segments. With beta != 0 the C loads are issued
+    // before the barrier and land while the partials are summed.
     const long long cbase = (long long)m0 * p.ldc + n0;
     const __amdgpu_buffer_rsrc_t rc =
         make_rsrc(Cb + cbase, (long long)(p.M - 1) * p.ldc + p.N - cbase);
-    const bool col_ok = n0 + lane < p.N;
+    const int col = lane % BN, sub = lane / BN;
+    const bool col_ok = n0 + col < p.N;
     uint32_t off[RPT];
 #pragma unroll
     for (int r = 0; r < RPT; ++r) {
-        const int row = wave + WAVES * r;
-        off[r] = (col_ok && m0 + row < p.M) ? (uint32_t)(((long long)row * p.ldc + lane) * 4)
+        const int row = RPW * (wave + WAVES * r) + sub;
+        off[r] = (col_ok && m0 + row < p.M) ? (uint32_t)(((long long)row * p.ldc + col) * 4)
                                             : kOOB;
     }
     const bool with_beta = p.beta != 0.0f;
@@ -927,11 +931,11 @@ sgemm_stream_kernel(Params p)
     __syncthreads();
 #pragma unroll
     for (int r = 0; r < RPT; ++r) {
-        const int row = wave + WAVES * r;
-        float x = lds[row * PITCH + lane];
+        const int row = RPW * (wave + WAVES * r) + sub;
+        float x = lds[row * PITCH + col];
 #pragma unroll
         for (int w = 1; w < WAVES; ++w)
-            x += lds[(w * BM + row) * PITCH + lane];
+            x += lds[(w * BM + row) * PITCH + col];
         store1(rc, off[r], with_beta ? p.alpha * x + p.beta * cin[r] : p.alpha * x);
     }
 }
@@ -1201,14 +1205,14 @@ constexpr VariantInfo make_dma_variant()
                          sgemm_dma_kernel<BM, BN, WM_, WN_, MW, false, true>}}};
 }
 
-template <int WAVES, int STAGES, int BM, int MINW>
+template <int WAVES, int STAGES, int BM, int BN, int MINW>
 constexpr VariantInfo make_stream_variant()
 {
-    return VariantInfo{BM, 64, 16, 64 * WAVES, 4,
-                       {{sgemm_stream_kernel<WAVES, STAGES, BM, MINW, true, false>,
-                         sgemm_stream_kernel<WAVES, STAGES, BM, MINW, true, true>},
-                        {sgemm_stream_kernel<WAVES, STAGES, BM, MINW, false, false>,
-                         sgemm_stream_kernel<WAVES, STAGES, BM, MINW, false, true>}}};
+    return VariantInfo{BM, BN, 16, 64 * WAVES, 4,
+                       {{sgemm_stream_kernel<WAVES, STAGES, BM, BN, MINW, true, false>,
+                         sgemm_stream_kernel<WAVES, STAGES, BM, BN, MINW, true, true>},
+                        {sgemm_stream_kernel<WAVES, STAGES, BM, BN, MINW, false, false>,
+                         sgemm_stream_kernel<WAVES, STAGES, BM, BN, MINW, false, true>}}};
 }
 
 const VariantInfo kVariants[SGEMM_VARIANT_COUNT] = {
@@ -1216,11 +1220,12 @@ const VariantInfo kVariants[SGEMM_VARIANT_COUNT] = {
     make_variant<128, 128, kBK, 2, 2, 1, 2, 4>(), // SGEMM_VARIANT_M128x128
     make_variant<64, 64, kBK, 2, 2, 1, 4, 4>(),   // SGEMM_VARIANT_S64x64
     make_variant<64, 64, kBK, 2, 2, 1, 4, 1>(),   // SGEMM_VARIANT_S64x64_V1
-    make_stream_variant<4, 4, 64, 1>(),           // SGEMM_VARIANT_T64x64
+    make_stream_variant<4, 4, 64, 64, 1>(),       // SGEMM_VARIANT_T64x64
     make_variant<256, 256, kBK, 2, 4, 1, 2, 4>(), // SGEMM_VARIANT_L256x256
     make_variant<64, 64, 32, 2, 2, 2, 2, 4>(),    // SGEMM_VARIANT_S64x64_K2
     make_dma_variant<128, 128, 2, 2, 2>(),        // SGEMM_VARIANT_M128x128_DMA
-    make_stream_variant<8, 3, 32, 2>(),           // SGEMM_VARIANT_T32x64
+    make_stream_variant<8, 3, 32, 64, 2>(),       // SGEMM_VARIANT_T32x64
+    make_stream_variant<8, 3, 64, 32, 2>(),       // SGEMM_VARIANT_T64x32
 };
 
 long long ceil_div(long long a, long long b) { return (a + b - 1) / b; }
@@ -1229,7 +1234,8 @@ long long ceil_div(long long a, long long b) { return (a + b - 1) / b; }
 // workgroups.
 bool is_stream(int variant)
 {
-    return variant == SGEMM_VARIANT_T64x64 || variant == SGEMM_VARIANT_T32x64;
+    return variant == SGEMM_VARIANT_T64x64 || variant == SGEMM_VARIANT_T32x64 ||
+           variant == SGEMM_VARIANT_T64x32;
 }
 
 int num_cus_of_current_device(int *out)
@@ -1302,12 +1308,22 @@ extern "C" int sgemm_select_variant(int transA, int transB, int M, int N, int K,
     const long long cus = num_cus;
     const long long tiles64 = ceil_div(M, 64) * ceil_div(N, 64) * batch;
     const long long tiles32 = ceil_div(M, 32) * ceil_div(N, 64) * batch;
-    // At most one 32 x 64 tile per CU: the eight-wave streaming kernel on that
-    // tile. Such a call takes as long as one workgroup's tile, and this tile
-    // is half the 64 x 64 one, with two waves per SIMD on it (8192 x 64 x
+    const long long tiles6432 = ceil_div(M, 64) * ceil_div(N, 32) * batch;
+    // The eight-wave streaming kernel on a 64 x 32 or 32 x 64 tile: with at
+    // most one such tile per CU a call takes as long as one workgroup's tile,
+    // which is half a 64 x 64 tile with two waves per SIMD on it (8192 x 64 x
     // 4096: 37 µs against 59 µs for the K-split 64 x 64 tile; 512 x 512 x 384:
-    // 7.0 against 8.7 µs; 128^3: 5.3 against 6.0 µs).
-    if (tiles32 <= cus)
+    // 7.0 against 8.7 µs; 128^3: 5.3 against 6.0 µs). Over K >= 512 the 64 x 32
+    // tile is 2-5 % faster than the 32 x 64 one (512^3: 7.7 against 8.1 µs;
+    // 640 x 480 x 2000: 19.5 against 20.0 µs); below, the 32 x 64 tile is
+    // (128^3: 5.1 against 5.3 µs). With a single row (M <= 32) or column
+    // (N <= 32) of tiles over a deep K the matching tile is also the best for
+    // any number of them: the 64 x 64 tiles come in the same number and each
+    // takes longer (16384 x 1 x 4096: 44 µs against 64 µs).
+    const bool few6432 = tiles6432 <= cus;
+    if (M > 32 && (N <= 32 ? few6432 || K >= 512 : few6432 && K >= 512))
+        return SGEMM_VARIANT_T64x32;
+    if (tiles32 <= cus || (M <= 32 && K >= 512))
         return SGEMM_VARIANT_T32x64;
     // One skinny dimension (<= 64) over a deep K whose long operand is too
     // large to stay in the 256 MB Infinity Cache from one call to the next
@@ -1321,19 +1337,24 @@ extern "C" int sgemm_select_variant(int transA, int transB, int M, int N, int K,
     // Otherwise the tile whose busiest CU finishes first: a CU receives
     // ceil(tiles / CUs) tiles, each costing its area over the variant's
     // relative efficiency. The efficiencies are fitted to sweeps of every
-    // variant over 48 shapes (precision_gemm_amd/tune.py): 128 x 128 tiles
+    // variant over 72 shapes (precision_gemm_amd/tune.py): 128 x 128 tiles
     // 1.00; the K-split 64 x 64 tile 0.88, for K >= 768; plain 64 x 64 tiles
     // 0.85, or 1.05 for K <= 512, where a tile's fixed costs (the first loads,
     // the C stores) outweigh its short K loop and the small tiles, more of
-    // them resident per CU, overlap those costs better. The 256-row tiles and
-    // the direct-to-LDS 128 x 128 tile never won by more than the sweeps'
-    // noise on the shapes that matter, so they are left to explicit requests.
+    // them resident per CU, overlap those costs better; the streaming 64 x 32
+    // tile 0.78, for K >= 2048 (any value from 0.75 to 0.80 picks the same
+    // variants on the sweeps), whose small area fills the last round of tiles
+    // better (1152^2 x 4096: 100 µs against 118 µs for the K-split tile). The
+    // 256-row tiles and the direct-to-LDS 128 x 128 tile never won by more than
+    // the sweeps' noise on the shapes that matter, so they are left to
+    // explicit requests.
     // A tile whose grid would not fit one launch (more than 2^31 - 1
     // work-items per item along the tile axis) is skipped.
     struct Choice { int variant, bm, bn, eff_pct; long long min_k; };
     const Choice choices[] = {{SGEMM_VARIANT_M128x128, 128, 128, 100, 0},
                               {SGEMM_VARIANT_S64x64_K2, 64, 64, 88, 768},
-                              {SGEMM_VARIANT_S64x64, 64, 64, K <= 512 ? 105 : 85, 0}};
+                              {SGEMM_VARIANT_S64x64, 64, 64, K <= 512 ? 105 : 85, 0},
+                              {SGEMM_VARIANT_T64x32, 64, 32, 78, 2048}};
     int best = SGEMM_VARIANT_M128x128;
     double best_cost = -1.0;
     for (const Choice &c : choices) {
@@ -1431,6 +1452,8 @@ struct Split {
     int splits;
 };
 
+int launch_canonical(const Call &c, int variant, hipStream_t s, Split sk);
+
 int launch(const Call &c, int variant, hipStream_t s, Split sk = Split{nullptr, 0, 1})
 {
     if (c.M == 0 || c.N == 0 || c.batch == 0)
@@ -1450,6 +1473,25 @@ int launch(const Call &c, int variant, hipStream_t s, Split sk = Split{nullptr, 
                                     dim3(256), args, 0, s);
     }
 
+    // A vector operand (M == 1 or N == 1) whose K elements are contiguous is
+    // the same memory in the k-contiguous description: op(B) with N == 1,
+    // transB == 0 and ldb == 1 is B[k], as with transB == 1 and any ldb >= K
+    // (likewise op(A) with M == 1, transA == 1, lda == 1). That description
+    // allows the 16-byte loads along k.
+    Call cc = c;
+    if (cc.N == 1 && cc.tB == 0 && cc.ldb == 1 && cc.K > 1 && cc.K <= kMaxLd) {
+        cc.tB = 1;
+        cc.ldb = cc.K;
+    }
+    if (cc.M == 1 && cc.tA == 1 && cc.lda == 1 && cc.K > 1 && cc.K <= kMaxLd) {
+        cc.tA = 0;
+        cc.lda = cc.K;
+    }
+    return launch_canonical(cc, variant, s, sk);
+}
+
+int launch_canonical(const Call &c, int variant, hipStream_t s, Split sk)
+{
     // 16-byte loads need aligned bases, ld and batch strides, and whole
     // 4-float chunks along each operand's contiguous dimension. Item pointers
     // of the pointer-array form are not visible here; the kernels check them.

@@ -1,7 +1,7 @@
 """Dispatch sweep: time every kernel variant on a grid of shapes and report how
 far the library's automatic choice is from the fastest one.
 
-    python -m precision_gemm_amd.tune [--shapes default|quick|wide] [--json out.json]
+    python -m precision_gemm_amd.tune [--shapes default|quick|wide|mid] [--json out.json]
     python -m precision_gemm_amd.tune --splitk [--json out.json]
 
 For each shape every applicable variant is timed on the same device buffers,
@@ -54,7 +54,7 @@ DEFAULT_SHAPES = [
 ]
 QUICK_SHAPES = [DEFAULT_SHAPES[i] for i in (3, 6, 10, 16, 19)]
 # Shapes the cost model was not fitted on: non-square, every transpose pair,
-# odd sizes, short K, batches.
+# odd sizes, short K, batches, and narrow products (one dimension 1 to 32).
 WIDE_SHAPES = [
     (1, 0, 4096, 4096, 4096, 1, 0.0), (0, 1, 4096, 4096, 4096, 1, 1.0),
     (1, 1, 4096, 4096, 4096, 1, 0.0), (0, 0, 3000, 3000, 3000, 1, 0.0),
@@ -68,6 +68,23 @@ WIDE_SHAPES = [
     (0, 0, 1024, 1024, 1024, 16, 0.0), (0, 0, 384, 768, 3072, 32, 0.0),
     (0, 1, 32768, 128, 4096, 1, 0.0), (0, 0, 128, 32768, 4096, 1, 0.0),
     (0, 0, 96, 96, 96, 1, 0.0), (0, 0, 640, 480, 2000, 1, 0.0),
+    (0, 0, 16384, 1, 4096, 1, 0.0), (0, 0, 16384, 16, 4096, 1, 0.0),
+    (0, 1, 65536, 32, 4096, 1, 0.0), (0, 0, 32, 16384, 4096, 1, 0.0),
+    (1, 0, 8, 65536, 2048, 1, 0.0), (0, 0, 4096, 24, 1024, 4, 0.0),
+]
+
+# Mid-size grids over deep K (one to five rounds of tiles), where the 64 x 32
+# streaming tile competes with the 64 x 64 tiles through the cost model.
+MID_SHAPES = [
+    (0, 0, 1536, 1536, 4096, 1, 0.0), (0, 0, 1536, 1536, 8192, 1, 0.0),
+    (0, 0, 1280, 1280, 4096, 1, 0.0), (0, 0, 1792, 1792, 4096, 1, 0.0),
+    (0, 0, 1536, 1536, 2048, 1, 0.0), (0, 0, 2048, 1024, 4096, 1, 0.0),
+    (0, 0, 1152, 1152, 4096, 1, 0.0), (0, 0, 1536, 1536, 3072, 1, 0.0),
+    (1, 0, 1536, 1536, 4096, 1, 0.0), (0, 1, 1536, 1536, 4096, 1, 0.0),
+    (0, 0, 1024, 1024, 8192, 1, 0.0), (0, 0, 2560, 2560, 4096, 1, 0.0),
+    (0, 0, 768, 768, 4096, 1, 0.0), (0, 0, 896, 896, 4096, 1, 0.0),
+    (0, 0, 1536, 768, 4096, 2, 0.0), (0, 0, 640, 640, 640, 1, 0.0),
+    (0, 0, 512, 256, 2048, 1, 0.0), (0, 0, 256, 256, 512, 2, 0.0),
 ]
 
 
@@ -195,7 +212,7 @@ def splitk_sweep(shapes, rounds: int = 3, target_ms: float = 20.0, out=sys.stdou
         v = pg.sgemm_select_variant(tA, tB, M, N, K, batch, 1, cus)
         # a streaming variant never splits; with a workspace the library swaps
         # in a 64 x 64 tile when splitting that pays
-        if v in (pg.VARIANT_T64x64, pg.VARIANT_T32x64):
+        if v in (pg.VARIANT_T64x64, pg.VARIANT_T32x64, pg.VARIANT_T64x32):
             vs = pg.VARIANT_S64x64_K2 if K >= 768 else pg.VARIANT_S64x64
         else:
             vs = v
@@ -237,7 +254,8 @@ def splitk_sweep(shapes, rounds: int = 3, target_ms: float = 20.0, out=sys.stdou
 
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
-    ap.add_argument("--shapes", choices=["default", "quick", "wide"], default="default")
+    ap.add_argument("--shapes", choices=["default", "quick", "wide", "mid"],
+                    default="default")
     ap.add_argument("--splitk", action="store_true",
                     help="compare the plain and split-K automatic calls on deep-K shapes")
     ap.add_argument("--rounds", type=int, default=3)
@@ -249,7 +267,8 @@ def main(argv=None) -> int:
             with open(args.json, "w") as f:
                 json.dump(res, f, indent=1)
         return 0
-    shapes = {"default": DEFAULT_SHAPES, "quick": QUICK_SHAPES, "wide": WIDE_SHAPES}[args.shapes]
+    shapes = {"default": DEFAULT_SHAPES, "quick": QUICK_SHAPES, "wide": WIDE_SHAPES,
+              "mid": MID_SHAPES}[args.shapes]
     res = sweep(shapes, rounds=args.rounds)
     regrets = [r["regret"] for r in res]
     print(f"shapes {len(res)}: mean regret {100 * statistics.mean(regrets):.2f} %, "

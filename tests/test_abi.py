@@ -136,12 +136,25 @@ def test_select_variant(pg):
     for shape in ((1024, 1024, 1024), (3072, 3072, 3072), (1536, 1536, 1536),
                   (1024, 1024, 4096), (1000, 1000, 1000)):
         assert sel(0, 0, *shape, 1, True, 256) == pg.VARIANT_S64x64_K2, shape
-    # at most one 32 x 64 tile per CU: the eight-wave streaming tile, skinny
-    # or not, whatever K (512 x 512: 128 tiles; 1024 x 512: 256)
+    # at most one tile per CU: the eight-wave streaming kernel, skinny or not,
+    # on its 64 x 32 tile over K >= 512 (512 x 512: 128 tiles; 1024 x 512:
+    # 256), on the 32 x 64 one below
     for shape in ((512, 512, 512), (512, 512, 8192), (1024, 512, 1024), (128, 128, 2048),
-                  (512, 512, 256), (96, 96, 384), (128, 128, 128), (256, 256, 16),
                   (8192, 64, 4096), (64, 8192, 4096), (4096, 128, 4096), (64, 8192, 8192)):
+        assert sel(0, 0, *shape, 1, True, 256) == pg.VARIANT_T64x32, shape
+    for shape in ((512, 512, 256), (96, 96, 384), (128, 128, 128), (256, 256, 16)):
         assert sel(0, 0, *shape, 1, True, 256) == pg.VARIANT_T32x64, shape
+    # N <= 32 < M: the 64 x 32 tile for small grids or any grid over K >= 512;
+    # M <= 32 with K >= 512: the 32 x 64 tile on any grid
+    for shape in ((16384, 1, 4096), (65536, 32, 4096), (4096, 8, 256), (100, 32, 64)):
+        assert sel(0, 0, *shape, 1, True, 256) == pg.VARIANT_T64x32, shape
+    # a last round of tiles that the 64 x 32 tile fills better (cost model)
+    for shape in ((1152, 1152, 4096), (1536, 1536, 4096), (1536, 1536, 8192)):
+        assert sel(0, 0, *shape, 1, True, 256) == pg.VARIANT_T64x32, shape
+    assert sel(0, 0, 1536, 1536, 1536, 1, True, 256) == pg.VARIANT_S64x64_K2
+    for shape in ((1, 16384, 4096), (32, 65536, 4096), (16, 16, 4096), (32, 32, 32)):
+        assert sel(0, 0, *shape, 1, True, 256) == pg.VARIANT_T32x64, shape
+    assert sel(0, 0, 32768, 16, 256, 1, True, 256) != pg.VARIANT_T64x32    # 512 tiles, short K
     assert sel(0, 0, 1024, 512, 1024, 1, True, 128) != pg.VARIANT_T32x64   # two per CU
     assert sel(0, 0, 512, 512, 128, 3, True, 256) != pg.VARIANT_T32x64     # 384 tiles
     assert sel(0, 0, 512, 512, 2048, 8, True, 256) == pg.VARIANT_S64x64_K2
@@ -229,6 +242,7 @@ def test_split_arguments_checked(pg):
                    **kw) == -21
     assert ws_call(pg, variant=pg.VARIANT_T64x64, splits=4, ws=(FAKE, 1 << 20), **kw) == -19
     assert ws_call(pg, variant=pg.VARIANT_T32x64, splits=4, ws=(FAKE, 1 << 20), **kw) == -19
+    assert ws_call(pg, variant=pg.VARIANT_T64x32, splits=4, ws=(FAKE, 1 << 20), **kw) == -19
     for st in (-19, -20, -21):
         assert "invalid" in pg.sgemm_status_string(st) or "too small" in \
             pg.sgemm_status_string(st)
@@ -266,15 +280,26 @@ _dim = st.integers(min_value=1, max_value=1 << 16)
 def test_select_variant_is_always_a_kernel(pg, tA, tB, M, N, K, batch, vec4, cus):
     """Any valid shape gets a variant in range; without 4-float loads it is the
     1-float variant; the 64 x 64 streaming kernel only for a dimension of at
-    most 64, the 32 x 64 one exactly for grids of at most one tile per CU."""
+    most 64; the 64 x 32 one for M > 32 with at most one tile per CU and
+    K >= 512, or N <= 32 with one tile per CU or K >= 512; otherwise the
+    32 x 64 one exactly for grids of at most one tile per CU or M <= 32 with
+    K >= 512."""
     v = pg.sgemm_select_variant(tA, tB, M, N, K, batch, vec4, cus)
     assert 0 <= v < pg.VARIANT_COUNT
     if not vec4:
         assert v == pg.VARIANT_S64x64_V1
     if v == pg.VARIANT_T64x64:
         assert min(M, N) <= 64 and K >= 512
-    small = -(-M // 32) * -(-N // 64) * batch <= cus
-    assert (v == pg.VARIANT_T32x64) == (vec4 and small)
+    few6432 = -(-M // 64) * -(-N // 32) * batch <= cus
+    t6432 = M > 32 and (few6432 or K >= 512 if N <= 32 else few6432 and K >= 512)
+    t3264 = -(-M // 32) * -(-N // 64) * batch <= cus or (M <= 32 and K >= 512)
+    if vec4 and t6432:
+        assert v == pg.VARIANT_T64x32
+    elif vec4 and t3264:
+        assert v == pg.VARIANT_T32x64
+    else:
+        # beyond those rules the 64 x 32 tile only from the cost model, K >= 2048
+        assert v != pg.VARIANT_T32x64 and (v != pg.VARIANT_T64x32 or K >= 2048)
     assert v not in (pg.VARIANT_L256x128, pg.VARIANT_L256x256, pg.VARIANT_M128x128_DMA)
 
 

@@ -181,11 +181,24 @@ def sweep_shapes(n, seed):
     return sorted(shapes)
 
 
+def canonical_vectors(tA, tB, M, N, K, lda, ldb):
+    """A vector operand whose k elements are adjacent (op(B) with N == 1, B
+    untransposed, ldb == 1; op(A) with M == 1, A transposed, lda == 1) is
+    described k-contiguous, the same memory, as the library does before it
+    picks the load width."""
+    if N == 1 and tB == 0 and ldb == 1 and 1 < K < 1 << 21:
+        tB, ldb = 1, K
+    if M == 1 and tA == 1 and lda == 1 and 1 < K < 1 << 21:
+        tA, lda = 0, K
+    return tA, tB, lda, ldb
+
+
 def vec4_possible(w):
-    a_kc, b_kc = w.trans_a == 0, w.trans_b == 1
+    tA, tB, lda, ldb = canonical_vectors(w.trans_a, w.trans_b, w.M, w.N, w.K, w.LDA, w.LDB)
+    a_kc, b_kc = tA == 0, tB == 1
     return ((w.K % 4 == 0) if a_kc else (w.M % 4 == 0)) and \
            ((w.K % 4 == 0) if b_kc else (w.N % 4 == 0)) and \
-           w.LDA % 4 == 0 and w.LDB % 4 == 0 and w.SA % 4 == 0 and w.SB % 4 == 0
+           lda % 4 == 0 and ldb % 4 == 0 and w.SA % 4 == 0 and w.SB % 4 == 0
 
 
 @pytest.mark.parametrize("variant", ALL_VARIANTS)
@@ -269,7 +282,7 @@ def random_shapes(n, seed):
 
 def test_automatic_dispatch_random_shapes(env):
     """120 seeded shapes through the automatic dispatch (every rule: the
-    32 x 64 streaming tile, the K-split and plain 64 x 64 tiles, the 128 x 128
+    32 x 64 and 64 x 32 streaming tiles, the K-split and plain 64 x 64 tiles, the 128 x 128
     tile, the 1-float variant), each checked against the oracle on its first
     and last rows of every batch item, and for writes outside C's windows."""
     torch, pg = env
@@ -284,10 +297,10 @@ def test_automatic_dispatch_random_shapes(env):
         for rows in ((0, min(w.M, 6)), (max(0, w.M - 3), w.M)):
             check_against_oracle(w, A, B, C, got, rows=rows)
         check_untouched(w, C, got)
-        vec4 = (w.LDA % 4 == 0 and w.LDB % 4 == 0 and vec4_possible(w))
+        vec4 = vec4_possible(w)
         seen.add(pg.sgemm_select_variant(w.trans_a, w.trans_b, w.M, w.N, w.K, w.batch,
                                          1 if vec4 else 0, cus))
-    for v in (pg.VARIANT_T32x64, pg.VARIANT_S64x64, pg.VARIANT_S64x64_K2,
+    for v in (pg.VARIANT_T32x64, pg.VARIANT_T64x32, pg.VARIANT_S64x64, pg.VARIANT_S64x64_K2,
               pg.VARIANT_M128x128, pg.VARIANT_S64x64_V1):
         assert v in seen, f"no shape reached {pg.VARIANT_NAMES[v]}"
 
@@ -582,6 +595,30 @@ def test_degenerate_shapes(env, shape):
         check_against_oracle(w, A, B, C, got, exact=True)
 
 
+@pytest.mark.parametrize("M,N,K", [(16384, 1, 4096), (1, 16384, 4096), (1, 1, 4096),
+                                   (300, 1, 1028), (1, 200, 36), (4096, 1, 2)])
+def test_vector_operand_descriptions_agree(env, M, N, K):
+    """A vector operand whose k elements are adjacent has two descriptions of
+    the same memory: op(B) with N == 1 as B untransposed with ldb == 1 or
+    transposed with ldb == K; op(A) with M == 1 as A transposed with lda == 1
+    or untransposed with lda == K. Every description gives the same bits,
+    within the oracle's bound."""
+    base = Workload("vec", 0, 1, M, N, K, 1.0, 0.5, seed=7 * M + N + K, ldb=K)
+    A, B, C = workloads.make_inputs(base)
+    outs = []
+    for tA in ((0, 1) if M == 1 else (0,)):
+        for tB in ((0, 1) if N == 1 else (1,)):
+            w = Workload("vec", tA, tB, M, N, K, 1.0, 0.5, seed=0, lda=1 if tA else K,
+                         ldb=K if tB else 1)
+            log(f"[vector] {'NT'[tA]}{'NT'[tB]} {M}x{N}x{K} lda={w.LDA} ldb={w.LDB}")
+            st, got = run_gpu(env, w, A, B, C)
+            assert st == 0
+            check_against_oracle(w, A, B, C, got)
+            outs.append(got)
+    for got in outs[1:]:
+        assert np.array_equal(got.view(np.uint32), outs[0].view(np.uint32))
+
+
 # ------------------------------------------------------------------ pointer-array batched
 
 def run_pointer_array(env, tA, tB, M, N, K, alpha, beta, lda, ldb, ldc, batch, seed, dist,
@@ -820,7 +857,8 @@ def run_gpu_ws(env, w: Workload, A, B, C, variant=-1, splits=0, ws_floats=None):
 
 # every tile kernel (not the streaming ones, which split K across their own waves)
 SPLIT_VARIANTS = [v for v in ALL_VARIANTS
-                  if v not in (pg_constants.VARIANT_T64x64, pg_constants.VARIANT_T32x64)]
+                  if v not in (pg_constants.VARIANT_T64x64, pg_constants.VARIANT_T32x64,
+                               pg_constants.VARIANT_T64x32)]
 
 
 @pytest.mark.parametrize("variant", SPLIT_VARIANTS)
