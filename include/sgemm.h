@@ -119,7 +119,10 @@ enum sgemm_variant {
     SGEMM_VARIANT_T64x32 = 9,   /*  64 x  32 tile, the same kernel (grids of at most one
                                     such tile per CU over K >= 512, N <= 32, or a last
                                     round of tiles it fills better) */
-    SGEMM_VARIANT_COUNT = 10
+    SGEMM_VARIANT_GEMV = 10,    /*  matrix-vector kernel without MFMA: N == 1 (or M == 1)
+                                    with transA == 0 and transB == 1 (both operands
+                                    contiguous in k); -18 for any other call */
+    SGEMM_VARIANT_COUNT = 11
 };
 
 /*
@@ -127,7 +130,12 @@ enum sgemm_variant {
  * the variant sgemm_strided_batched would launch for this shape, given
  * whether the 4-float load path is allowed (`vec4_ok`, see Alignment above)
  * and the device's compute-unit count. Returns an sgemm_variant, or a
- * negative status for invalid dimensions.
+ * negative status for invalid dimensions. The flags are those of the call
+ * after one normalization the entry points make first: a vector operand whose
+ * k elements are adjacent is described contiguous in k (op(B) with N == 1,
+ * transB == 0 and ldb == 1 as transB == 1, ldb == K; op(A) with M == 1,
+ * transA == 1 and lda == 1 as transA == 0, lda == K; for 1 < K < 2^21), which
+ * names the same memory.
  */
 int sgemm_select_variant(int transA, int transB, int M, int N, int K, int batch,
                          int vec4_ok, int num_cus);
@@ -242,7 +250,7 @@ size_t sgemm_workspace_size(int transA, int transB, int M, int N, int K, int bat
  * fewer than S slices can result). A forced split needs its full workspace
  * (-21 otherwise) and a tile variant (-19 for the streaming variants
  * SGEMM_VARIANT_T64x64, SGEMM_VARIANT_T32x64 and SGEMM_VARIANT_T64x32, which
- * split K across their own waves instead).
+ * split K across their own waves instead, and for SGEMM_VARIANT_GEMV).
  */
 int sgemm_strided_batched_ws_variant(int transA, int transB, int M, int N, int K,
                                      float alpha, const float *A, int lda,

@@ -22,7 +22,7 @@ __all__ = [
     "sgemm_status_string", "sgemm_select_variant", "matmul", "library_path",
     "VARIANT_AUTO", "VARIANT_L256x128", "VARIANT_M128x128", "VARIANT_S64x64",
     "VARIANT_S64x64_V1", "VARIANT_T64x64", "VARIANT_L256x256", "VARIANT_S64x64_K2",
-    "VARIANT_M128x128_DMA", "VARIANT_T32x64", "VARIANT_T64x32", "VARIANT_COUNT", "VARIANT_NAMES",
+    "VARIANT_M128x128_DMA", "VARIANT_T32x64", "VARIANT_T64x32", "VARIANT_GEMV", "VARIANT_COUNT", "VARIANT_NAMES",
 ]
 
 VARIANT_AUTO = -1
@@ -36,10 +36,11 @@ VARIANT_S64x64_K2 = 6
 VARIANT_M128x128_DMA = 7
 VARIANT_T32x64 = 8
 VARIANT_T64x32 = 9
-VARIANT_COUNT = 10
+VARIANT_GEMV = 10
+VARIANT_COUNT = 11
 VARIANT_NAMES = {0: "L256x128", 1: "M128x128", 2: "S64x64", 3: "S64x64_V1", 4: "T64x64",
                  5: "L256x256", 6: "S64x64_K2", 7: "M128x128_DMA",
-                 8: "T32x64", 9: "T64x32"}
+                 8: "T32x64", 9: "T64x32", 10: "GEMV"}
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _lib = None

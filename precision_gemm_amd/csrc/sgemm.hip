@@ -1132,6 +1132,100 @@ sgemm_dma_kernel(Params p)
     store_tile<TM, TN, 16>(p, Cb, m0, n0, wm0, wn0, 0, lane, res);
 }
 
+// Matrix-vector product, the N == 1 case with both operands contiguous in k:
+// y[m] = alpha * sum_k A[m, k] x[k] + beta * y[m], A's rows lda apart, x the K
+// floats of op(B), y[m] at C[m * ldc]. It moves K floats of A per output and
+// does two flops per float, far below the MFMA ridge, so it is plain FMAs at
+// the HBM rate. A workgroup owns ROWS rows; its 256 threads take the 4-float
+// chunks of k round-robin, keeping UNROLL chunks of every row in flight, and
+// the partial sums are added across each wave with lane exchanges and across
+// the four waves in LDS, always in the same order.
+// 16-byte load through the global address space (the item pointers arrive
+// as generic pointers, which would otherwise become flat loads).
+__device__ __forceinline__ f32x4 global_load4(const float *q)
+{
+    return *(const __attribute__((address_space(1))) f32x4 *)q;
+}
+
+template <int ROWS>
+__global__ void __launch_bounds__(256) sgemv_kernel(Params p)
+{
+    constexpr int T = 256, UNROLL = 4, WAVES = T / 64;
+    const int b = blockIdx.y;
+    const int m0 = blockIdx.x * ROWS;
+    const int t = threadIdx.x;
+    const float *A = item_a(p, b), *x = item_b(p, b);
+    float *C = item_c(p, b);
+    // Rows past M read row M - 1 again; their sums are dropped.
+    const float *row[ROWS];
+#pragma unroll
+    for (int r = 0; r < ROWS; ++r)
+        row[r] = A + (long long)min(m0 + r, p.M - 1) * p.lda;
+    float acc[ROWS];
+#pragma unroll
+    for (int r = 0; r < ROWS; ++r)
+        acc[r] = 0.0f;
+    if (((uintptr_t)A | (uintptr_t)x) & 15u) {
+        // An item of the pointer-array form off 16-byte alignment.
+        for (int k = t; k < p.K; k += T) {
+            const float xv = x[k];
+#pragma unroll
+            for (int r = 0; r < ROWS; ++r)
+                acc[r] = fmaf(row[r][k], xv, acc[r]);
+        }
+    } else {
+        const int K4 = p.K >> 2; // the host guarantees K % 4 == 0 and lda % 4 == 0
+        auto dot4 = [](const f32x4 &a, const f32x4 &v, float s) {
+            s = fmaf(a[0], v[0], s);
+            s = fmaf(a[1], v[1], s);
+            s = fmaf(a[2], v[2], s);
+            return fmaf(a[3], v[3], s);
+        };
+        int c = t;
+        for (; c + (UNROLL - 1) * T < K4; c += UNROLL * T) {
+            f32x4 xv[UNROLL], av[UNROLL][ROWS];
+#pragma unroll
+            for (int u = 0; u < UNROLL; ++u) {
+                xv[u] = global_load4(x + 4 * (c + u * T));
+#pragma unroll
+                for (int r = 0; r < ROWS; ++r)
+                    av[u][r] = global_load4(row[r] + 4 * (c + u * T));
+            }
+#pragma unroll
+            for (int u = 0; u < UNROLL; ++u)
+#pragma unroll
+                for (int r = 0; r < ROWS; ++r)
+                    acc[r] = dot4(av[u][r], xv[u], acc[r]);
+        }
+        for (; c < K4; c += T) {
+            const f32x4 xv = global_load4(x + 4 * c);
+#pragma unroll
+            for (int r = 0; r < ROWS; ++r)
+                acc[r] = dot4(global_load4(row[r] + 4 * c), xv, acc[r]);
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < ROWS; ++r)
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1)
+            acc[r] += __shfl_xor(acc[r], off);
+    __shared__ float part[WAVES][ROWS];
+    if ((t & 63) == 0) {
+#pragma unroll
+        for (int r = 0; r < ROWS; ++r)
+            part[t >> 6][r] = acc[r];
+    }
+    __syncthreads();
+    if (t < ROWS && m0 + t < p.M) {
+        float sum = part[0][t];
+#pragma unroll
+        for (int w = 1; w < WAVES; ++w)
+            sum += part[w][t];
+        float *y = C + (long long)(m0 + t) * p.ldc;
+        *y = p.beta == 0.0f ? p.alpha * sum : p.alpha * sum + p.beta * *y;
+    }
+}
+
 // C = beta * C over the M x N window of every batch item (alpha == 0 or K == 0).
 __global__ void __launch_bounds__(256) sgemm_scale_kernel(float *C, float *const *Carr, int M,
                                                           int N, int ldc, long long sC,
@@ -1226,6 +1320,9 @@ const VariantInfo kVariants[SGEMM_VARIANT_COUNT] = {
     make_dma_variant<128, 128, 2, 2, 2>(),        // SGEMM_VARIANT_M128x128_DMA
     make_stream_variant<8, 3, 32, 64, 2>(),       // SGEMM_VARIANT_T32x64
     make_stream_variant<8, 3, 64, 32, 2>(),       // SGEMM_VARIANT_T64x32
+    // SGEMM_VARIANT_GEMV: N == 1 (or M == 1, as its transpose) with op(A) and
+    // op(B) contiguous in k; four rows per workgroup (one on small grids).
+    VariantInfo{4, 1, 4, 256, 4, {{nullptr, sgemv_kernel<4>}, {nullptr, nullptr}}},
 };
 
 long long ceil_div(long long a, long long b) { return (a + b - 1) / b; }
@@ -1237,6 +1334,9 @@ bool is_stream(int variant)
     return variant == SGEMM_VARIANT_T64x64 || variant == SGEMM_VARIANT_T32x64 ||
            variant == SGEMM_VARIANT_T64x32;
 }
+
+// Variants that never split K across workgroups.
+bool no_split(int variant) { return is_stream(variant) || variant == SGEMM_VARIANT_GEMV; }
 
 int num_cus_of_current_device(int *out)
 {
@@ -1303,6 +1403,13 @@ extern "C" int sgemm_select_variant(int transA, int transB, int M, int N, int K,
     if (batch < 0) return -14;
     if (!vec4_ok)
         return SGEMM_VARIANT_S64x64_V1;
+    // A matrix-vector product (N == 1, or M == 1 as its transpose) with both
+    // operands contiguous in k: the GEMV kernel, which streams the matrix
+    // without the 32 columns of MFMA work a tile would do per output
+    // (4096 x 1 x 4096: 34 µs on the 64 x 32 tile, whose 64 workgroups leave
+    // most CUs idle).
+    if (transA == 0 && transB == 1 && (N == 1 || M == 1))
+        return SGEMM_VARIANT_GEMV;
     if (num_cus < 1)
         num_cus = 1;
     const long long cus = num_cus;
@@ -1421,7 +1528,7 @@ extern "C" int sgemm_select_splits(int transA, int transB, int M, int N, int K, 
     if (batch < 0) return -14;
     if (variant < 0 || variant >= SGEMM_VARIANT_COUNT)
         return -18;
-    if (is_stream(variant))
+    if (no_split(variant))
         return 1;
     int kslice = 0;
     return (int)splits_for(variant, M, N, K, batch, num_cus < 1 ? 1 : num_cus, &kslice);
@@ -1490,6 +1597,66 @@ int launch(const Call &c, int variant, hipStream_t s, Split sk = Split{nullptr, 
     return launch_canonical(cc, variant, s, sk);
 }
 
+// The GEMV kernel over every batch item of an N == 1 call whose op(A) and
+// op(B) are contiguous in k.
+int launch_gemv(const Call &c, hipStream_t s)
+{
+    int cus = 0;
+    const int st = num_cus_of_current_device(&cus);
+    if (st != 0)
+        return st;
+    // Four rows per workgroup, or one when that leaves fewer than two
+    // workgroups per CU.
+    const int rows = ceil_div(c.M, 4) * c.batch >= 2LL * cus ? 4 : 1;
+    const long long blocks = ceil_div(c.M, rows);
+    if (blocks * 256 > INT32_MAX)
+        return -22;
+    const KernelFn fn = rows == 4 ? sgemv_kernel<4> : sgemv_kernel<1>;
+    Params p{};
+    p.A = c.A;
+    p.B = c.B;
+    p.C = c.C;
+    p.Aarr = c.Aarr;
+    p.Barr = c.Barr;
+    p.Carr = c.Carr;
+    p.M = c.M;
+    p.N = 1;
+    p.K = c.K;
+    p.lda = c.lda;
+    p.ldb = c.ldb;
+    p.ldc = c.ldc;
+    p.sA = c.sA;
+    p.sB = c.sB;
+    p.sC = c.sC;
+    p.alpha = c.alpha;
+    p.beta = c.beta;
+    p.tiles_m = (int)blocks;
+    p.tiles_n = 1;
+    p.group_m = 1;
+    p.splits = 1;
+    p.kslice = c.K;
+    const bool arrays = c.Aarr != nullptr;
+    for (long long b0 = 0; b0 < c.batch; b0 += 65535) {
+        const long long nb = c.batch - b0 < 65535 ? c.batch - b0 : 65535;
+        Params q = p;
+        if (arrays) {
+            q.Aarr = c.Aarr + b0;
+            q.Barr = c.Barr + b0;
+            q.Carr = c.Carr + b0;
+        } else {
+            q.A = c.A + b0 * c.sA;
+            q.B = c.B + b0 * c.sB;
+            q.C = c.C + b0 * c.sC;
+        }
+        void *args[] = {&q};
+        hipError_t e = hipLaunchKernel((const void *)fn, dim3((unsigned)blocks, (unsigned)nb),
+                                       dim3(256), args, 0, s);
+        if (e != hipSuccess)
+            return (int)e;
+    }
+    return 0;
+}
+
 int launch_canonical(const Call &c, int variant, hipStream_t s, Split sk)
 {
     // 16-byte loads need aligned bases, ld and batch strides, and whole
@@ -1515,6 +1682,29 @@ int launch_canonical(const Call &c, int variant, hipStream_t s, Split sk)
     } else if (kVariants[variant].vec == 4 && !vec4_ok) {
         return -18;
     }
+    if (variant == SGEMM_VARIANT_GEMV) {
+        if (c.tA != 0 || c.tB != 1 || (c.N != 1 && c.M != 1))
+            return -18;
+        if (sk.splits >= 2)
+            return -19;
+        if (c.N == 1)
+            return launch_gemv(c, s);
+        // M == 1: the transpose, C^T (N x 1, rows 1 apart) = op(B)^T op(A)^T,
+        // whose matrix is B (N x K, rows ldb apart) and whose vector is A's row.
+        Call t = c;
+        t.M = c.N;
+        t.N = 1;
+        t.A = c.B;
+        t.B = c.A;
+        t.Aarr = c.Barr;
+        t.Barr = c.Aarr;
+        t.lda = c.ldb;
+        t.ldb = c.lda;
+        t.sA = c.sB;
+        t.sB = c.sA;
+        t.ldc = 1;
+        return launch_gemv(t, s);
+    }
 
     // Split-K: the tile kernels write per-slice partial tiles into the
     // workspace and a second kernel sums them in slice order.
@@ -1522,7 +1712,7 @@ int launch_canonical(const Call &c, int variant, hipStream_t s, Split sk)
     int splits = 1, kslice = c.K;
     if (sk.splits == 0 && sk.ws != nullptr) {
         int v = variant;
-        long long S = is_stream(v) ? 1 : splits_for(v, c.M, c.N, c.K, c.batch, cus, &kslice);
+        long long S = no_split(v) ? 1 : splits_for(v, c.M, c.N, c.K, c.batch, cus, &kslice);
         if (auto_variant && is_stream(v)) {
             // A grid too small even for the streaming kernel's CUs: split the
             // 64 x 64 tile across workgroups instead.
@@ -1551,7 +1741,7 @@ int launch_canonical(const Call &c, int variant, hipStream_t s, Split sk)
             kslice = c.K;
         }
     } else if (sk.splits >= 2) {
-        if (is_stream(variant))
+        if (no_split(variant))
             return -19;
         const int bk = kVariants[variant].bk;
         const long long ks = ceil_div(ceil_div(c.K, sk.splits), bk) * bk;
@@ -1757,7 +1947,7 @@ extern "C" size_t sgemm_workspace_size(int transA, int transB, int M, int N, int
     // 64 x 64 tile that replaces the streaming kernel on tiny grids.
     const int v = sgemm_select_variant(transA, transB, M, N, K, batch, 1, cus);
     int kslice = 0;
-    long long S = is_stream(v) ? 1 : splits_for(v, M, N, K, batch, cus, &kslice);
+    long long S = no_split(v) ? 1 : splits_for(v, M, N, K, batch, cus, &kslice);
     const long long S2 = splits_for(SGEMM_VARIANT_S64x64, M, N, K, batch, cus, &kslice);
     if (is_stream(v) && S2 > S)
         S = S2;

@@ -128,7 +128,17 @@ def sweep(shapes, rounds: int = 3, target_ms: float = 20.0, out=sys.stdout):
         lda, ldb = A.shape[2], B.shape[2]
         sa, sb, sc = A.stride(0), B.stride(0), C.stride(0)
         auto = pg.sgemm_select_variant(tA, tB, M, N, K, batch, 1, cus)
-        variants = [v for v in range(pg.VARIANT_COUNT) if v != pg.VARIANT_S64x64_V1]
+        # The GEMV kernel takes only N == 1 or M == 1 with both operands
+        # contiguous in k, after the library describes a stride-1 vector
+        # operand that way.
+        cA, cB = tA, tB
+        if N == 1 and tB == 0 and ldb == 1 and 1 < K < 1 << 21:
+            cB = 1
+        if M == 1 and tA == 1 and lda == 1 and 1 < K < 1 << 21:
+            cA = 0
+        gemv_ok = cA == 0 and cB == 1 and (M == 1 or N == 1)
+        variants = [v for v in range(pg.VARIANT_COUNT) if v != pg.VARIANT_S64x64_V1 and
+                    (v != pg.VARIANT_GEMV or gemv_ok)]
 
         def caller(v):
             return lambda: pg.sgemm_strided_batched_variant(

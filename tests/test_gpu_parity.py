@@ -23,8 +23,10 @@ from workloads import Workload
 
 pytestmark = pytest.mark.gpu
 
-# every kernel variant (the enum of the C header, mirrored by the binding)
-ALL_VARIANTS = list(range(pg_constants.VARIANT_COUNT))
+# every kernel variant that takes any shape (the enum of the C header,
+# mirrored by the binding); the GEMV kernel, which only takes N == 1 or M == 1,
+# has tests of its own
+ALL_VARIANTS = [v for v in range(pg_constants.VARIANT_COUNT) if v != pg_constants.VARIANT_GEMV]
 
 GUARD = 64  # floats of canary before and after each device buffer (keeps 256-B alignment)
 
@@ -619,6 +621,77 @@ def test_vector_operand_descriptions_agree(env, M, N, K):
         assert np.array_equal(got.view(np.uint32), outs[0].view(np.uint32))
 
 
+# ------------------------------------------------------------------ the GEMV kernel
+
+def gemv_cases():
+    """(name, tA, tB, M, N, K, lda, ldb, ldc, batch) for the GEMV kernel: N == 1
+    and its mirror M == 1, in the k-contiguous description and in the stride-1
+    vector description the library converts; row counts on both sides of the
+    four-rows-per-workgroup choice; K with and without a partial unrolled pass."""
+    out = []
+    for L in (1, 2, 3, 5, 63, 257, 1000, 4099):
+        for K in (4, 12, 1028, 4100):
+            if L * K > 6_000_000:
+                continue
+            pad = 4 if (L + K) % 3 == 0 else 0
+            out.append((f"n1_{L}x{K}", 0, 1, L, 1, K, K + pad, K, 1 + (L % 3), 1))
+            out.append((f"m1_{L}x{K}", 0, 1, 1, L, K, K, K + pad, L, 1))
+    for L, K in ((300, 1028), (1000, 260)):
+        out.append((f"n1_vec_{L}x{K}", 0, 0, L, 1, K, K, 1, 1, 3))
+        out.append((f"m1_vec_{L}x{K}", 1, 1, 1, L, K, 1, K + 4, L, 3))
+    return out
+
+
+@pytest.mark.parametrize("variant", [-1, pg_constants.VARIANT_GEMV])
+def test_gemv_bitwise(env, variant):
+    """The GEMV kernel, auto-dispatched and forced, on integer inputs: bitwise
+    equal to the oracle, nothing outside C's windows touched."""
+    _, pg = env
+    for i, (name, tA, tB, M, N, K, lda, ldb, ldc, batch) in enumerate(gemv_cases()):
+        alpha, beta = ((1.0, 0.0), (-2.0, 0.5), (0.5, -1.0))[i % 3]
+        w = Workload(name, tA, tB, M, N, K, alpha, beta, seed=500 + i, dist="int3",
+                     lda=lda, ldb=ldb, ldc=ldc, batch=batch)
+        A, B, C = workloads.make_inputs(w)
+        log(f"[gemv] variant {variant} {name} batch={batch}")
+        st, got = run_gpu(env, w, A, B, C, variant=variant)
+        assert st == 0, (name, st)
+        check_against_oracle(w, A, B, C, got, exact=True)
+        check_untouched(w, C, got)
+
+
+@pytest.mark.parametrize("M,N,K", [(16384, 1, 4096), (4096, 1, 4096), (1, 16384, 4096),
+                                   (1024, 1, 65536)])
+def test_gemv_float_at_size(env, M, N, K):
+    """U(-1, 1) inputs at the sizes the kernel is for, checked against the
+    oracle's bound on rows from both ends (for M == 1, the whole row)."""
+    _, pg = env
+    w = Workload("gemv_f", 0, 1, M, N, K, 1.0, 0.5, seed=M + N + K)
+    A, B, C = workloads.make_inputs(w)
+    assert pg.sgemm_select_variant(0, 1, M, N, K, 1, 1, 256) == pg.VARIANT_GEMV
+    st, got = run_gpu(env, w, A, B, C)
+    assert st == 0
+    if M == 1:
+        check_against_oracle(w, A, B, C, got)
+    else:
+        for rows in ((0, 64), (M // 2, M // 2 + 64), (M - 64, M)):
+            check_against_oracle(w, A, B, C, got, rows=rows)
+    check_untouched(w, C, got)
+
+
+def test_gemv_refuses_other_calls(env):
+    """Forced on a call it does not cover, the GEMV variant returns -18, and
+    it never splits K (-19)."""
+    _, pg = env
+    for tA, tB, M, N, K in ((0, 0, 64, 64, 64), (0, 1, 64, 2, 64), (1, 1, 64, 1, 64),
+                            (0, 0, 64, 1, 64)):
+        w = Workload("gemv_no", tA, tB, M, N, K, 1.0, 0.0, seed=1,
+                     ldb=(K if tB else N) + (8 if (tA, tB, N) == (0, 0, 1) else 0))
+        A, B, C = workloads.make_inputs(w)
+        st, got = run_gpu(env, w, A, B, C, variant=pg.VARIANT_GEMV)
+        assert st == -18, (tA, tB, M, N, K, st)
+        assert np.array_equal(got.view(np.uint32), C.view(np.uint32))
+
+
 # ------------------------------------------------------------------ pointer-array batched
 
 def run_pointer_array(env, tA, tB, M, N, K, alpha, beta, lda, ldb, ldc, batch, seed, dist,
@@ -700,6 +773,18 @@ def test_pointer_array_bitwise(env, variant):
                                     variant=variant)
         assert st == 0, st
         check_items(tA, tB, M, N, K, 2.0, -1.0, lda, ldb, ldc, res, exact=True)
+
+
+def test_pointer_array_gemv(env):
+    """Pointer-array batches through the GEMV kernel (N == 1 and M == 1):
+    items off 16-byte alignment take its plain path; all exact."""
+    for tA, tB, M, N, K, lda, ldb, ldc in ((0, 1, 300, 1, 132, 136, 132, 2),
+                                           (0, 1, 1, 260, 68, 68, 72, 260)):
+        st, res = run_pointer_array(env, tA, tB, M, N, K, 1.5, -0.5, lda, ldb, ldc, batch=5,
+                                    seed=41 + M, dist="int3", misalign=(1, 3), shared_a=(4,),
+                                    variant=pg_constants.VARIANT_GEMV)
+        assert st == 0, st
+        check_items(tA, tB, M, N, K, 1.5, -0.5, lda, ldb, ldc, res, exact=True)
 
 
 @pytest.mark.parametrize("variant", [-1, 0, 2, 4, 5, 6, 7])
