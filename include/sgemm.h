@@ -119,9 +119,10 @@ enum sgemm_variant {
     SGEMM_VARIANT_T64x32 = 9,   /*  64 x  32 tile, the same kernel (grids of at most one
                                     such tile per CU over K >= 512, N <= 32, or a last
                                     round of tiles it fills better) */
-    SGEMM_VARIANT_GEMV = 10,    /*  matrix-vector kernel without MFMA: N == 1 (or M == 1)
-                                    with transA == 0 and transB == 1 (both operands
-                                    contiguous in k); -18 for any other call */
+    SGEMM_VARIANT_GEMV = 10,    /*  matrix-vector kernels without MFMA: N == 1 with
+                                    transB == 1, or M == 1 with transA == 0 (the vector
+                                    contiguous in k), the matrix either way; -18 for
+                                    any other call */
     SGEMM_VARIANT_COUNT = 11
 };
 

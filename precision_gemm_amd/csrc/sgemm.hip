@@ -1226,6 +1226,96 @@ __global__ void __launch_bounds__(256) sgemv_kernel(Params p)
     }
 }
 
+__device__ __forceinline__ float global_load1(const float *q)
+{
+    return *(const __attribute__((address_space(1))) float *)q;
+}
+
+// Matrix-vector product with the matrix contiguous along the outputs, the
+// N == 1 case with A stored K x M: y[m] = alpha * sum_k A[k * lda + m] x[k] +
+// beta * y[m], x the K floats of op(B), y[m] at C[m * ldc]. A workgroup owns
+// BC outputs. A load instruction of a wave covers RPI = 256 / BC consecutive
+// rows, BC / 4 lanes of 16 bytes per row; the eight waves take turns of RPI
+// rows each, UNROLL loads in flight. The partial sums are added across the
+// lanes of a column group, then across the waves in LDS, in a fixed order.
+template <int BC>
+__global__ void __launch_bounds__(512) sgemv_t_kernel(Params p)
+{
+    constexpr int WAVES = 8, LPR = BC / 4, RPI = 64 / LPR, UNROLL = 8, STEP = WAVES * RPI;
+    const int b = blockIdx.y;
+    // Neighbouring column blocks share 128-byte lines: each XCD (workgroup
+    // pid runs on XCD pid % 8) gets a contiguous range of blocks.
+    const int num = gridDim.x, pid = blockIdx.x;
+    const int xcd = pid % kNumXcd, local = pid / kNumXcd;
+    const int q = num / kNumXcd, r = num % kNumXcd;
+    const int blk = xcd < r ? xcd * (q + 1) + local : r * (q + 1) + (xcd - r) * q + local;
+    const int m0 = blk * BC;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int cg = lane % LPR, ro = lane / LPR;
+    const int m = m0 + 4 * cg; // the host guarantees M % 4 == 0 and lda % 4 == 0
+    const float *A = item_a(p, b), *x = item_b(p, b);
+    float *C = item_c(p, b);
+    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (m < p.M) {
+        const float *col = A + m;
+        int k = wave * RPI + ro;
+        if (((uintptr_t)A | (uintptr_t)x) & 15u) {
+            // An item of the pointer-array form off 16-byte alignment.
+            for (; k < p.K; k += STEP) {
+                const float xv = x[k];
+                const float *a = col + (long long)k * p.lda;
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    acc[j] = fmaf(a[j], xv, acc[j]);
+            }
+        } else {
+            const int kfull = p.K - (UNROLL - 1) * STEP; // k < kfull: all UNROLL rows exist
+            for (; k < kfull; k += UNROLL * STEP) {
+                f32x4 av[UNROLL];
+                float xv[UNROLL];
+#pragma unroll
+                for (int u = 0; u < UNROLL; ++u) {
+                    av[u] = global_load4(col + (long long)(k + u * STEP) * p.lda);
+                    xv[u] = global_load1(x + k + u * STEP);
+                }
+#pragma unroll
+                for (int u = 0; u < UNROLL; ++u)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        acc[j] = fmaf(av[u][j], xv[u], acc[j]);
+            }
+            for (; k < p.K; k += STEP) {
+                const f32x4 av = global_load4(col + (long long)k * p.lda);
+                const float xv = global_load1(x + k);
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    acc[j] = fmaf(av[j], xv, acc[j]);
+            }
+        }
+    }
+#pragma unroll
+    for (int off = LPR; off < 64; off <<= 1)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            acc[j] += __shfl_xor(acc[j], off);
+    __shared__ f32x4 part[WAVES][LPR];
+    if (ro == 0)
+        part[wave][cg] = acc;
+    __syncthreads();
+    const int t = threadIdx.x;
+    if (t < LPR && m0 + 4 * t < p.M) {
+        f32x4 sum = part[0][t];
+#pragma unroll
+        for (int w = 1; w < WAVES; ++w)
+            sum += part[w][t];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            float *y = C + (long long)(m0 + 4 * t + j) * p.ldc;
+            *y = p.beta == 0.0f ? p.alpha * sum[j] : p.alpha * sum[j] + p.beta * *y;
+        }
+    }
+}
+
 // C = beta * C over the M x N window of every batch item (alpha == 0 or K == 0).
 __global__ void __launch_bounds__(256) sgemm_scale_kernel(float *C, float *const *Carr, int M,
                                                           int N, int ldc, long long sC,
@@ -1320,9 +1410,9 @@ const VariantInfo kVariants[SGEMM_VARIANT_COUNT] = {
     make_dma_variant<128, 128, 2, 2, 2>(),        // SGEMM_VARIANT_M128x128_DMA
     make_stream_variant<8, 3, 32, 64, 2>(),       // SGEMM_VARIANT_T32x64
     make_stream_variant<8, 3, 64, 32, 2>(),       // SGEMM_VARIANT_T64x32
-    // SGEMM_VARIANT_GEMV: N == 1 (or M == 1, as its transpose) with op(A) and
-    // op(B) contiguous in k; four rows per workgroup (one on small grids).
-    VariantInfo{4, 1, 4, 256, 4, {{nullptr, sgemv_kernel<4>}, {nullptr, nullptr}}},
+    // SGEMM_VARIANT_GEMV: N == 1 (or M == 1, as its transpose) with the vector
+    // contiguous in k; launched by launch_gemv, which picks the kernel.
+    VariantInfo{4, 1, 4, 256, 4, {{nullptr, sgemv_kernel<4>}, {nullptr, sgemv_t_kernel<64>}}},
 };
 
 long long ceil_div(long long a, long long b) { return (a + b - 1) / b; }
@@ -1403,12 +1493,12 @@ extern "C" int sgemm_select_variant(int transA, int transB, int M, int N, int K,
     if (batch < 0) return -14;
     if (!vec4_ok)
         return SGEMM_VARIANT_S64x64_V1;
-    // A matrix-vector product (N == 1, or M == 1 as its transpose) with both
-    // operands contiguous in k: the GEMV kernel, which streams the matrix
+    // A matrix-vector product (N == 1, or M == 1 as its transpose) whose
+    // vector is contiguous in k: the GEMV kernels, which stream the matrix
     // without the 32 columns of MFMA work a tile would do per output
     // (4096 x 1 x 4096: 34 µs on the 64 x 32 tile, whose 64 workgroups leave
-    // most CUs idle).
-    if (transA == 0 && transB == 1 && (N == 1 || M == 1))
+    // most CUs idle, against 11 µs).
+    if ((N == 1 && transB == 1) || (M == 1 && transA == 0))
         return SGEMM_VARIANT_GEMV;
     if (num_cus < 1)
         num_cus = 1;
@@ -1597,21 +1687,38 @@ int launch(const Call &c, int variant, hipStream_t s, Split sk = Split{nullptr, 
     return launch_canonical(cc, variant, s, sk);
 }
 
-// The GEMV kernel over every batch item of an N == 1 call whose op(A) and
-// op(B) are contiguous in k.
+// The GEMV kernels over every batch item of an N == 1 call whose op(B) is
+// contiguous in k: op(A) contiguous in k (transA == 0) or along M.
 int launch_gemv(const Call &c, hipStream_t s)
 {
     int cus = 0;
     const int st = num_cus_of_current_device(&cus);
     if (st != 0)
         return st;
-    // Four rows per workgroup, or one when that leaves fewer than two
-    // workgroups per CU.
-    const int rows = ceil_div(c.M, 4) * c.batch >= 2LL * cus ? 4 : 1;
-    const long long blocks = ceil_div(c.M, rows);
-    if (blocks * 256 > INT32_MAX)
+    long long blocks;
+    int threads;
+    KernelFn fn;
+    if (c.tA == 0) {
+        // Four rows per workgroup, or one when that leaves fewer than two
+        // workgroups per CU.
+        const int rows = ceil_div(c.M, 4) * c.batch >= 2LL * cus ? 4 : 1;
+        blocks = ceil_div(c.M, rows);
+        threads = 256;
+        fn = rows == 4 ? sgemv_kernel<4> : sgemv_kernel<1>;
+    } else {
+        // The widest block of outputs (64, 32 or 16: row segments of 256, 128
+        // or 64 bytes) that still gives every CU a workgroup, else 16
+        // (16384 x 1 x 4096: 38 µs with 64, 44 with 32, 50 with 16; 8192 x 1 x
+        // 8192: 42, 40, 48 µs; 4096 x 1 x 4096: 20, 15, 14 µs).
+        const int bc = ceil_div(c.M, 64) * c.batch >= cus   ? 64
+                       : ceil_div(c.M, 32) * c.batch >= cus ? 32
+                                                            : 16;
+        blocks = ceil_div(c.M, bc);
+        threads = 512;
+        fn = bc == 64 ? sgemv_t_kernel<64> : bc == 32 ? sgemv_t_kernel<32> : sgemv_t_kernel<16>;
+    }
+    if (blocks * threads > INT32_MAX)
         return -22;
-    const KernelFn fn = rows == 4 ? sgemv_kernel<4> : sgemv_kernel<1>;
     Params p{};
     p.A = c.A;
     p.B = c.B;
@@ -1650,7 +1757,7 @@ int launch_gemv(const Call &c, hipStream_t s)
         }
         void *args[] = {&q};
         hipError_t e = hipLaunchKernel((const void *)fn, dim3((unsigned)blocks, (unsigned)nb),
-                                       dim3(256), args, 0, s);
+                                       dim3(threads), args, 0, s);
         if (e != hipSuccess)
             return (int)e;
     }
@@ -1683,17 +1790,20 @@ int launch_canonical(const Call &c, int variant, hipStream_t s, Split sk)
         return -18;
     }
     if (variant == SGEMM_VARIANT_GEMV) {
-        if (c.tA != 0 || c.tB != 1 || (c.N != 1 && c.M != 1))
+        if (!((c.N == 1 && c.tB == 1) || (c.M == 1 && c.tA == 0)))
             return -18;
         if (sk.splits >= 2)
             return -19;
-        if (c.N == 1)
+        if (c.N == 1 && c.tB == 1)
             return launch_gemv(c, s);
         // M == 1: the transpose, C^T (N x 1, rows 1 apart) = op(B)^T op(A)^T,
-        // whose matrix is B (N x K, rows ldb apart) and whose vector is A's row.
+        // whose matrix is op(B)^T (B with the other transpose flag) and whose
+        // vector is A's row.
         Call t = c;
         t.M = c.N;
         t.N = 1;
+        t.tA = 1 - c.tB;
+        t.tB = 1;
         t.A = c.B;
         t.B = c.A;
         t.Aarr = c.Barr;

@@ -144,13 +144,17 @@ def test_select_variant(pg):
         assert sel(0, 0, *shape, 1, True, 256) == pg.VARIANT_T64x32, shape
     for shape in ((512, 512, 256), (96, 96, 384), (128, 128, 128), (256, 256, 16)):
         assert sel(0, 0, *shape, 1, True, 256) == pg.VARIANT_T32x64, shape
-    # a matrix-vector product with both operands contiguous in k (transA 0,
-    # transB 1): the GEMV kernel, for N == 1 and for M == 1, whatever the size
+    # a matrix-vector product whose vector is contiguous in k (N == 1 with B
+    # transposed, M == 1 with A not): the GEMV kernels, the matrix either way
     for shape in ((16384, 1, 4096), (1, 16384, 4096), (1, 1, 4), (7, 1, 100000), (1, 3, 8)):
         assert sel(0, 1, *shape, 1, True, 256) == pg.VARIANT_GEMV, shape
         assert sel(0, 1, *shape, 1, False, 256) == pg.VARIANT_S64x64_V1, shape
-    for tA, tB in ((0, 0), (1, 0), (1, 1)):
+    assert sel(1, 1, 16384, 1, 4096, 1, True, 256) == pg.VARIANT_GEMV
+    assert sel(0, 0, 1, 16384, 4096, 1, True, 256) == pg.VARIANT_GEMV
+    for tA, tB in ((0, 0), (1, 0)):
         assert sel(tA, tB, 16384, 1, 4096, 1, True, 256) != pg.VARIANT_GEMV
+    for tA, tB in ((1, 0), (1, 1)):
+        assert sel(tA, tB, 1, 16384, 4096, 1, True, 256) != pg.VARIANT_GEMV
     assert sel(0, 1, 16384, 2, 4096, 1, True, 256) != pg.VARIANT_GEMV
     # N <= 32 < M: the 64 x 32 tile for small grids or any grid over K >= 512;
     # M <= 32 with K >= 512: the 32 x 64 tile on any grid
@@ -160,7 +164,7 @@ def test_select_variant(pg):
     for shape in ((1152, 1152, 4096), (1536, 1536, 4096), (1536, 1536, 8192)):
         assert sel(0, 0, *shape, 1, True, 256) == pg.VARIANT_T64x32, shape
     assert sel(0, 0, 1536, 1536, 1536, 1, True, 256) == pg.VARIANT_S64x64_K2
-    for shape in ((1, 16384, 4096), (32, 65536, 4096), (16, 16, 4096), (32, 32, 32)):
+    for shape in ((2, 16384, 4096), (32, 65536, 4096), (16, 16, 4096), (32, 32, 32)):
         assert sel(0, 0, *shape, 1, True, 256) == pg.VARIANT_T32x64, shape
     assert sel(0, 0, 32768, 16, 256, 1, True, 256) != pg.VARIANT_T64x32    # 512 tiles, short K
     assert sel(0, 0, 1024, 512, 1024, 1, True, 128) != pg.VARIANT_T32x64   # two per CU
@@ -291,8 +295,8 @@ _dim = st.integers(min_value=1, max_value=1 << 16)
        batch=st.integers(1, 512), vec4=st.booleans(), cus=st.integers(1, 512))
 def test_select_variant_is_always_a_kernel(pg, tA, tB, M, N, K, batch, vec4, cus):
     """Any valid shape gets a variant in range; without 4-float loads it is the
-    1-float variant; with them, the GEMV kernel exactly for N == 1 or M == 1
-    with both operands contiguous in k; the 64 x 64 streaming kernel only for
+    1-float variant; with them, the GEMV kernels exactly for N == 1 with B
+    transposed or M == 1 with A not (the vector contiguous in k); the 64 x 64 streaming kernel only for
     a dimension of at most 64; the 64 x 32 one for M > 32 with at most one tile per CU and
     K >= 512, or N <= 32 with one tile per CU or K >= 512; otherwise the
     32 x 64 one exactly for grids of at most one tile per CU or M <= 32 with
@@ -306,7 +310,7 @@ def test_select_variant_is_always_a_kernel(pg, tA, tB, M, N, K, batch, vec4, cus
     few6432 = -(-M // 64) * -(-N // 32) * batch <= cus
     t6432 = M > 32 and (few6432 or K >= 512 if N <= 32 else few6432 and K >= 512)
     t3264 = -(-M // 32) * -(-N // 64) * batch <= cus or (M <= 32 and K >= 512)
-    gemv = tA == 0 and tB == 1 and (M == 1 or N == 1)
+    gemv = (N == 1 and tB == 1) or (M == 1 and tA == 0)
     if vec4 and gemv:
         assert v == pg.VARIANT_GEMV
     elif vec4 and t6432:

@@ -624,10 +624,12 @@ def test_vector_operand_descriptions_agree(env, M, N, K):
 # ------------------------------------------------------------------ the GEMV kernel
 
 def gemv_cases():
-    """(name, tA, tB, M, N, K, lda, ldb, ldc, batch) for the GEMV kernel: N == 1
-    and its mirror M == 1, in the k-contiguous description and in the stride-1
-    vector description the library converts; row counts on both sides of the
-    four-rows-per-workgroup choice; K with and without a partial unrolled pass."""
+    """(name, tA, tB, M, N, K, lda, ldb, ldc, batch) for the GEMV kernels: N == 1
+    and its mirror M == 1; the matrix contiguous in k (any row count) or along
+    the outputs (counts that are multiples of 4); the vector in the
+    k-contiguous description and in the stride-1 description the library
+    converts; counts on both sides of each kernel's workgroup-size choice; K
+    with and without a partial unrolled pass."""
     out = []
     for L in (1, 2, 3, 5, 63, 257, 1000, 4099):
         for K in (4, 12, 1028, 4100):
@@ -636,6 +638,18 @@ def gemv_cases():
             pad = 4 if (L + K) % 3 == 0 else 0
             out.append((f"n1_{L}x{K}", 0, 1, L, 1, K, K + pad, K, 1 + (L % 3), 1))
             out.append((f"m1_{L}x{K}", 0, 1, 1, L, K, K, K + pad, L, 1))
+    for L in (4, 8, 60, 256, 1000, 4100):
+        for K in (4, 36, 1028, 1100):
+            if L * K > 6_000_000:
+                continue
+            pad = 4 if (L + K) % 3 == 0 else 0
+            out.append((f"n1t_{L}x{K}", 1, 1, L, 1, K, L + pad, K, 1 + (L % 3), 1))
+            out.append((f"m1t_{L}x{K}", 0, 0, 1, L, K, K, L + pad, L, 1))
+    # the 64- and 32-wide column blocks (enough of them for a workgroup per CU)
+    out.append(("n1t_64", 1, 1, 16384, 1, 68, 16388, 68, 1, 1))
+    out.append(("m1t_64", 0, 0, 1, 4096, 132, 132, 4100, 4096, 4))
+    out.append(("n1t_32", 1, 1, 8192, 1, 36, 8192, 36, 2, 1))
+    out.append(("m1t_32", 0, 0, 1, 2048, 100, 100, 2052, 2048, 4))
     for L, K in ((300, 1028), (1000, 260)):
         out.append((f"n1_vec_{L}x{K}", 0, 0, L, 1, K, K, 1, 1, 3))
         out.append((f"m1_vec_{L}x{K}", 1, 1, 1, L, K, 1, K + 4, L, 3))
@@ -659,15 +673,17 @@ def test_gemv_bitwise(env, variant):
         check_untouched(w, C, got)
 
 
-@pytest.mark.parametrize("M,N,K", [(16384, 1, 4096), (4096, 1, 4096), (1, 16384, 4096),
-                                   (1024, 1, 65536)])
-def test_gemv_float_at_size(env, M, N, K):
-    """U(-1, 1) inputs at the sizes the kernel is for, checked against the
+@pytest.mark.parametrize("tA,tB,M,N,K", [(0, 1, 16384, 1, 4096), (0, 1, 4096, 1, 4096),
+                                         (0, 1, 1, 16384, 4096), (0, 1, 1024, 1, 65536),
+                                         (1, 1, 16384, 1, 4096), (1, 1, 4096, 1, 4096),
+                                         (0, 0, 1, 16384, 4096), (1, 1, 1024, 1, 65536)])
+def test_gemv_float_at_size(env, tA, tB, M, N, K):
+    """U(-1, 1) inputs at the sizes the kernels are for, checked against the
     oracle's bound on rows from both ends (for M == 1, the whole row)."""
     _, pg = env
-    w = Workload("gemv_f", 0, 1, M, N, K, 1.0, 0.5, seed=M + N + K)
+    w = Workload("gemv_f", tA, tB, M, N, K, 1.0, 0.5, seed=M + N + K + tA + tB)
     A, B, C = workloads.make_inputs(w)
-    assert pg.sgemm_select_variant(0, 1, M, N, K, 1, 1, 256) == pg.VARIANT_GEMV
+    assert pg.sgemm_select_variant(tA, tB, M, N, K, 1, 1, 256) == pg.VARIANT_GEMV
     st, got = run_gpu(env, w, A, B, C)
     assert st == 0
     if M == 1:
@@ -682,7 +698,7 @@ def test_gemv_refuses_other_calls(env):
     """Forced on a call it does not cover, the GEMV variant returns -18, and
     it never splits K (-19)."""
     _, pg = env
-    for tA, tB, M, N, K in ((0, 0, 64, 64, 64), (0, 1, 64, 2, 64), (1, 1, 64, 1, 64),
+    for tA, tB, M, N, K in ((0, 0, 64, 64, 64), (0, 1, 64, 2, 64), (1, 0, 2, 64, 64),
                             (0, 0, 64, 1, 64)):
         w = Workload("gemv_no", tA, tB, M, N, K, 1.0, 0.0, seed=1,
                      ldb=(K if tB else N) + (8 if (tA, tB, N) == (0, 0, 1) else 0))
@@ -779,7 +795,9 @@ def test_pointer_array_gemv(env):
     """Pointer-array batches through the GEMV kernel (N == 1 and M == 1):
     items off 16-byte alignment take its plain path; all exact."""
     for tA, tB, M, N, K, lda, ldb, ldc in ((0, 1, 300, 1, 132, 136, 132, 2),
-                                           (0, 1, 1, 260, 68, 68, 72, 260)):
+                                           (0, 1, 1, 260, 68, 68, 72, 260),
+                                           (1, 1, 300, 1, 132, 304, 132, 2),
+                                           (0, 0, 1, 260, 68, 68, 264, 260)):
         st, res = run_pointer_array(env, tA, tB, M, N, K, 1.5, -0.5, lda, ldb, ldc, batch=5,
                                     seed=41 + M, dist="int3", misalign=(1, 3), shared_a=(4,),
                                     variant=pg_constants.VARIANT_GEMV)
