@@ -8,6 +8,9 @@ kernels in tests/probes, built by __graft_entry__.build()).
   probe runs one MFMA on integer operands and checks every register.
 - The FP32 MFMA issue rate: long runs of independent MFMAs with no memory
   traffic, reported against the 157.3 TFLOP/s dense FP32-MFMA peak.
+- Both FP32 MFMA shapes (32x32x2 and 16x16x4), with four independent
+  accumulators per wave and with one dependent chain: the rates each shape
+  sustains and what a dependent chain costs.
 """
 import ctypes
 import os
@@ -34,6 +37,9 @@ def probes():
     lib.probe_mfma_tflops.restype = ctypes.c_int
     lib.probe_mfma_tflops.argtypes = [ctypes.c_int, ctypes.c_int, p,
                                       ctypes.POINTER(ctypes.c_double)]
+    lib.probe_mfma_shape_tflops.restype = ctypes.c_int
+    lib.probe_mfma_shape_tflops.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                            p, ctypes.POINTER(ctypes.c_double)]
     return torch, lib
 
 
@@ -73,6 +79,28 @@ def test_mfma_issue_rate(probes):
     sys.stdout.flush()
     # a sanity floor only: the rate depends on the clock the device runs at
     assert tf.value > 0.5 * 157.3 * cus / 256
+
+
+def test_mfma_shapes(probes):
+    torch, lib = probes
+    dev = torch.device("cuda:0")
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    out = torch.empty(cus * 256, dtype=torch.float32, device=dev)
+    rates = {}
+    # one workgroup of four waves per CU: one wave per SIMD, so a dependent
+    # chain is not hidden behind another wave
+    for shape in (32, 16):
+        for chains in (4, 1):
+            tf = ctypes.c_double(0.0)
+            assert lib.probe_mfma_shape_tflops(shape, chains, cus, 4096 if shape == 32 else 8192,
+                                               out.data_ptr(), ctypes.byref(tf)) == 0
+            rates[shape, chains] = tf.value
+            sys.stdout.write(f"{shape}x{shape}x{128 // shape / 2:.0f} MFMA, {chains} chain(s): "
+                             f"{tf.value:.1f} TFLOP/s ({100 * tf.value / 157.3:.1f} % of 157.3)\n")
+    sys.stdout.flush()
+    assert lib.probe_mfma_shape_tflops(8, 4, 1, 1, out.data_ptr(), ctypes.byref(tf)) == -1
+    for v in rates.values():
+        assert v > 0.1 * 157.3 * cus / 256
 
 
 def test_no_schedule_cliff_across_transposes():
