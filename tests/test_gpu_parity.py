@@ -529,14 +529,22 @@ def test_matmul_tensor_wrapper(env):
 
 # ------------------------------------------------------------------ extremes
 
-def test_batch_beyond_one_launch(env):
-    """More batch items than one launch's second grid axis holds (65535)."""
-    w = Workload("manybatch", 0, 1, 4, 8, 12, 1.0, -1.0, seed=21, dist="int3", batch=70000)
+@pytest.mark.parametrize("tA,tB,M,N", [(0, 1, 4, 8), (0, 1, 12, 1), (1, 1, 8, 1), (0, 0, 1, 8)])
+def test_batch_beyond_one_launch(env, tA, tB, M, N):
+    """More batch items than one launch's second grid axis holds (65535), for a
+    tile kernel and for both GEMV kernels (N == 1, and M == 1 through its
+    transpose)."""
+    _, pg = env
+    w = Workload("manybatch", tA, tB, M, N, 12, 1.0, -1.0, seed=21 + M + N, dist="int3",
+                 batch=70000)
     A, B, C = workloads.make_inputs(w)
+    gemv = pg.sgemm_select_variant(tA, tB, M, N, 12, 70000, 1, 256) == pg.VARIANT_GEMV
+    assert gemv == (M == 1 or N == 1)
     st, got = run_gpu(env, w, A, B, C)
     assert st == 0
     for b0, b1 in ((0, 3), (65534, 65537), (69997, 70000)):
         check_against_oracle(w, A, B, C, got, exact=True, batches=(b0, b1))
+    check_untouched(w, C, got)
 
 
 @pytest.mark.parametrize("which", ["lda", "ldb", "ldc"])

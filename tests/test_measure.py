@@ -49,3 +49,27 @@ def test_mi355x_workload_rooflines():
     # 70 % of FP32-MFMA peak at 4092^3 is 110.1 TFLOP/s, i.e. at most 1.2445 ms
     t = by["sgemm_4092"].flops() / (0.7 * measure.MI355X_FP32_MFMA_PEAK)
     assert t == pytest.approx(1.2445e-3, rel=1e-4)
+
+
+def test_bench_roofline_bound_follows_the_ridge():
+    """bench.py reports a call above the ridge against the FP32-MFMA peak and a
+    matrix-vector product (below it) against the HBM peak, in GB/s of
+    algorithmic bytes."""
+    import bench
+    peak, bw = measure.MI355X_FP32_MFMA_PEAK, measure.MI355X_HBM_BW
+    gemv = workloads.BY_NAME["gemv_16384x1x4096_nt"]
+    roof = measure.roofline(gemv.flops(), gemv.algorithmic_bytes(), peak, bw)
+    assert roof.bound == "memory-bound" and roof.intensity == pytest.approx(0.5, abs=0.01)
+    ms = 0.04
+    tflops = gemv.flops() / (ms * 1e-3) / 1e12
+    e = bench.roofline_entry(gemv, roof, tflops, peak / 1e12, ms, None)
+    assert (e["bound"], e["unit"], e["peak"]) == ("hbm", "GB/s", 8000.0)
+    assert e["achieved"] == pytest.approx(gemv.algorithmic_bytes() / (ms * 1e-3) / 1e9, rel=1e-3)
+    assert e["frac"] == pytest.approx(e["achieved"] / 8000.0, abs=1e-4)
+    big = workloads.BY_NAME["sgemm_4092"]
+    roof = measure.roofline(big.flops(), big.algorithmic_bytes(), peak, bw)
+    ms = 0.91
+    tflops = big.flops() / (ms * 1e-3) / 1e12
+    e = bench.roofline_entry(big, roof, tflops, peak / 1e12, ms, 123)
+    assert (e["bound"], e["unit"], e["traffic"]) == ("mfma", "TFLOP/s", 123)
+    assert e["achieved"] == pytest.approx(tflops, abs=1e-3)

@@ -155,5 +155,15 @@ CONFIGS: list[Workload] = [
              note="memory-streaming shape, B stored N x K"),
 ]
 
-BY_NAME = {w.name: w for w in CONFIGS}
+# Matrix-vector products, measured and profiled beside the five (not part of
+# them): y = A x with A's rows contiguous in k, and y = A^T x with A stored
+# K x M (contiguous along the outputs).
+EXTRA: list[Workload] = [
+    Workload("gemv_16384x1x4096_nt", 0, 1, 16384, 1, 4096, 1.0, 0.0, seed=6,
+             note="matrix-vector product, matrix rows contiguous in k"),
+    Workload("gemv_16384x1x4096_tt", 1, 1, 16384, 1, 4096, 1.0, 0.0, seed=7,
+             note="matrix-vector product, matrix contiguous along the outputs"),
+]
+
+BY_NAME = {w.name: w for w in CONFIGS + EXTRA}
 HEADLINE = BY_NAME["sgemm_4092"]
