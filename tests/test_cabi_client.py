@@ -142,6 +142,12 @@ CASES = [
     (ENTRY_POINTERS, Workload("c_pointers", 1, 1, 100, 72, 52, 1.5, -0.5, seed=35, batch=2)),
     (ENTRY_COLMAJOR, Workload("c_colmajor", 1, 0, 68, 132, 36, 0.5, 2.0, seed=36,
                               lda=68, ldb=132, ldc=72)),
+    # matrix-vector products: the GEMV kernels, row-major N == 1 and a
+    # column-major N == 1 call (its row-major twin has M == 1)
+    (ENTRY_SGEMM, Workload("c_gemv", 0, 1, 300, 1, 136, -1.5, 0.5, seed=37, lda=140, ldc=2)),
+    (ENTRY_STRIDED, Workload("c_gemv_t", 1, 1, 260, 1, 68, 1.0, 0.0, seed=38, batch=3)),
+    (ENTRY_COLMAJOR, Workload("c_colmajor_gemv", 0, 0, 260, 1, 68, 1.0, 0.5, seed=39,
+                              lda=264, ldb=68, ldc=260)),
 ]
 
 
