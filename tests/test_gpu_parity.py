@@ -265,9 +265,15 @@ def random_shapes(n, seed):
         else:
             M, N = (int(rng.integers(200, 3000)) for _ in range(2))
         K = int(np.exp(rng.uniform(0, np.log(6000))))
+        gemv = rng.random() < 0.1  # a matrix-vector product, either way round
+        if gemv:
+            if rng.random() < 0.5:
+                N = 1
+            else:
+                M = 1
         aligned = rng.random() < 0.75  # most real shapes are multiples of 4
         if aligned:
-            M, N, K = (max(4, x // 4 * 4) for x in (M, N, K))
+            M, N, K = (x if x == 1 and gemv else max(4, x // 4 * 4) for x in (M, N, K))
         batch = int(rng.choice([1, 1, 1, 2, 3, 8]))
         if M * N * batch > 4_000_000 or (M + N) * K * batch > 16_000_000:
             continue
@@ -283,8 +289,8 @@ def random_shapes(n, seed):
 
 
 def test_automatic_dispatch_random_shapes(env):
-    """120 seeded shapes through the automatic dispatch (every rule: the
-    32 x 64 and 64 x 32 streaming tiles, the K-split and plain 64 x 64 tiles, the 128 x 128
+    """120 seeded shapes through the automatic dispatch (every rule: the GEMV
+    kernels, the 32 x 64 and 64 x 32 streaming tiles, the K-split and plain 64 x 64 tiles, the 128 x 128
     tile, the 1-float variant), each checked against the oracle on its first
     and last rows of every batch item, and for writes outside C's windows."""
     torch, pg = env
@@ -300,10 +306,10 @@ def test_automatic_dispatch_random_shapes(env):
             check_against_oracle(w, A, B, C, got, rows=rows)
         check_untouched(w, C, got)
         vec4 = vec4_possible(w)
-        seen.add(pg.sgemm_select_variant(w.trans_a, w.trans_b, w.M, w.N, w.K, w.batch,
-                                         1 if vec4 else 0, cus))
+        tA, tB, _, _ = canonical_vectors(w.trans_a, w.trans_b, w.M, w.N, w.K, w.LDA, w.LDB)
+        seen.add(pg.sgemm_select_variant(tA, tB, w.M, w.N, w.K, w.batch, 1 if vec4 else 0, cus))
     for v in (pg.VARIANT_T32x64, pg.VARIANT_T64x32, pg.VARIANT_S64x64, pg.VARIANT_S64x64_K2,
-              pg.VARIANT_M128x128, pg.VARIANT_S64x64_V1):
+              pg.VARIANT_M128x128, pg.VARIANT_S64x64_V1, pg.VARIANT_GEMV):
         assert v in seen, f"no shape reached {pg.VARIANT_NAMES[v]}"
 
 
