@@ -155,7 +155,8 @@ def roofline_entry(w, roof, achieved_tflops, peak_tflops, per_launch_ms, traffic
                 "tflops_at_achieved": round(achieved_tflops, 3)}
     return {"bound": "mfma", "achieved": round(achieved_tflops, 3), "peak": peak_tflops,
             "unit": "TFLOP/s", "frac": round(achieved_tflops / peak_tflops, 4), **common,
-            "hbm_gbs_at_achieved": round(gbs, 1)}
+            "hbm_gbs_at_achieved": round(gbs, 1),
+            "hbm_frac_at_achieved": round(gbs * 1e9 / measure.MI355X_HBM_BW, 4)}
 
 
 def main(argv=None) -> int:

@@ -73,3 +73,4 @@ def test_bench_roofline_bound_follows_the_ridge():
     e = bench.roofline_entry(big, roof, tflops, peak / 1e12, ms, 123)
     assert (e["bound"], e["unit"], e["traffic"]) == ("mfma", "TFLOP/s", 123)
     assert e["achieved"] == pytest.approx(tflops, abs=1e-3)
+    assert e["hbm_frac_at_achieved"] == pytest.approx(e["hbm_gbs_at_achieved"] / 8000.0, abs=1e-4)
