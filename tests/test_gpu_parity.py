@@ -455,14 +455,17 @@ def test_concurrent_host_threads(env):
 def test_graph_capture_replays(env):
     """Calls captured into a HIP graph (the library only launches kernels on
     the caller's stream and allocates nothing) replay to the eager bits,
-    replay after replay, with other eager work in between: a T32x64 call, a
-    K-split tile call, and a split-K call whose reduction kernel is captured
-    too (workspace allocated before the capture)."""
+    replay after replay, with other eager work in between: a streaming-tile
+    call, a K-split tile call, a split-K call whose reduction kernel is
+    captured too (workspace allocated before the capture), and both GEMV
+    kernels."""
     torch, pg = env
     dev = torch.device("cuda:0")
     cases = [Workload("g_t32", 0, 1, 256, 192, 700, 1.0, 0.5, seed=51),
              Workload("g_k2", 1, 0, 1000, 1000, 1000, -1.0, 2.0, seed=52),
-             Workload("g_split", 0, 0, 128, 192, 8192, 0.5, 1.0, seed=53, batch=2)]
+             Workload("g_split", 0, 0, 128, 192, 8192, 0.5, 1.0, seed=53, batch=2),
+             Workload("g_gemv", 0, 1, 3000, 1, 1028, 1.5, 0.5, seed=54),
+             Workload("g_gemv_t", 1, 1, 2048, 1, 900, -1.0, 1.0, seed=55, batch=2)]
     bufs, want = [], []
     for w in cases:
         A, B, C = workloads.make_inputs(w)
@@ -490,7 +493,8 @@ def test_graph_capture_replays(env):
     torch.cuda.synchronize(dev)
     want = [dC.cpu().numpy().view(np.uint32).copy() for (_, _, _, _, dC, _) in bufs]
 
-    log("[graph] capture three calls")
+    assert pg.sgemm_select_variant(0, 1, 3000, 1, 1028, 1, 1, 256) == pg.VARIANT_GEMV
+    log(f"[graph] capture {len(bufs)} calls")
     g = torch.cuda.CUDAGraph()
     side = torch.cuda.Stream(dev)
     side.wait_stream(torch.cuda.current_stream(dev))
