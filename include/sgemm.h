@@ -121,8 +121,9 @@ enum sgemm_variant {
                                     round of tiles it fills better) */
     SGEMM_VARIANT_GEMV = 10,    /*  matrix-vector kernels without MFMA: N == 1 with
                                     transB == 1, or M == 1 with transA == 0 (the vector
-                                    contiguous in k), the matrix either way; -18 for
-                                    any other call */
+                                    contiguous in k), the matrix either way; or a few
+                                    vectors, 2 <= N <= 8, with transA == 0 (B either
+                                    way); -18 for any other call */
     SGEMM_VARIANT_COUNT = 11
 };
 

@@ -1226,6 +1226,111 @@ __global__ void __launch_bounds__(256) sgemv_kernel(Params p)
     }
 }
 
+// The same for a few vectors, 2 <= N <= NV: y[m, j] = alpha * sum_k A[m, k]
+// op(B)[k, j] + beta * y[m, j], y[m, j] at C[m * ldc + j]. op(B) is B's rows
+// (B_KC: B stored N x K, vector j at B + j * ldb) or B stored K x N (rows of N
+// floats ldb apart; N is then a multiple of 4 and NV == N). Each thread's
+// 4-float chunk of k of every row meets the same four k of every vector.
+template <int ROWS, int NV, bool B_KC>
+__global__ void __launch_bounds__(256) sgemv_nv_kernel(Params p)
+{
+    constexpr int T = 256, WAVES = T / 64;
+    const int b = blockIdx.y;
+    const int m0 = blockIdx.x * ROWS;
+    const int t = threadIdx.x;
+    const int N = p.N;
+    const float *A = item_a(p, b), *B = item_b(p, b);
+    float *C = item_c(p, b);
+    // Rows past M read row M - 1 again, vectors past N vector N - 1; those
+    // sums are dropped.
+    const float *row[ROWS];
+#pragma unroll
+    for (int r = 0; r < ROWS; ++r)
+        row[r] = A + (long long)min(m0 + r, p.M - 1) * p.lda;
+    float acc[ROWS][NV];
+#pragma unroll
+    for (int r = 0; r < ROWS; ++r)
+#pragma unroll
+        for (int j = 0; j < NV; ++j)
+            acc[r][j] = 0.0f;
+    if (((uintptr_t)A | (uintptr_t)B) & 15u) {
+        // An item of the pointer-array form off 16-byte alignment.
+        for (int k = t; k < p.K; k += T) {
+#pragma unroll
+            for (int j = 0; j < NV; ++j) {
+                const int jj = min(j, N - 1);
+                const float xv = B_KC ? B[(long long)jj * p.ldb + k] : B[(long long)k * p.ldb + jj];
+#pragma unroll
+                for (int r = 0; r < ROWS; ++r)
+                    acc[r][j] = fmaf(row[r][k], xv, acc[r][j]);
+            }
+        }
+    } else {
+        const int K4 = p.K >> 2; // the host guarantees K % 4 == 0 and lda % 4 == 0
+#pragma unroll 2
+        for (int c = t; c < K4; c += T) {
+            float x[4][NV];
+            if constexpr (B_KC) {
+#pragma unroll
+                for (int j = 0; j < NV; ++j) {
+                    const f32x4 v = global_load4(B + (long long)min(j, N - 1) * p.ldb + 4 * c);
+#pragma unroll
+                    for (int kk = 0; kk < 4; ++kk)
+                        x[kk][j] = v[kk];
+                }
+            } else {
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+                    for (int v = 0; v < NV / 4; ++v) {
+                        const f32x4 q = global_load4(B + (long long)(4 * c + kk) * p.ldb + 4 * v);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            x[kk][4 * v + e] = q[e];
+                    }
+            }
+            f32x4 av[ROWS];
+#pragma unroll
+            for (int r = 0; r < ROWS; ++r)
+                av[r] = global_load4(row[r] + 4 * c);
+#pragma unroll
+            for (int r = 0; r < ROWS; ++r)
+#pragma unroll
+                for (int j = 0; j < NV; ++j)
+#pragma unroll
+                    for (int kk = 0; kk < 4; ++kk)
+                        acc[r][j] = fmaf(av[r][kk], x[kk][j], acc[r][j]);
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < ROWS; ++r)
+#pragma unroll
+        for (int j = 0; j < NV; ++j)
+#pragma unroll
+            for (int off = 32; off > 0; off >>= 1)
+                acc[r][j] += __shfl_xor(acc[r][j], off);
+    __shared__ float part[WAVES][ROWS][NV];
+    if ((t & 63) == 0) {
+#pragma unroll
+        for (int r = 0; r < ROWS; ++r)
+#pragma unroll
+            for (int j = 0; j < NV; ++j)
+                part[t >> 6][r][j] = acc[r][j];
+    }
+    __syncthreads();
+    if (t < ROWS * NV) {
+        const int r = t / NV, j = t % NV;
+        if (m0 + r < p.M && j < N) {
+            float sum = part[0][r][j];
+#pragma unroll
+            for (int w = 1; w < WAVES; ++w)
+                sum += part[w][r][j];
+            float *y = C + (long long)(m0 + r) * p.ldc + j;
+            *y = p.beta == 0.0f ? p.alpha * sum : p.alpha * sum + p.beta * *y;
+        }
+    }
+}
+
 __device__ __forceinline__ float global_load1(const float *q)
 {
     return *(const __attribute__((address_space(1))) float *)q;
@@ -1503,6 +1608,17 @@ extern "C" int sgemm_select_variant(int transA, int transB, int M, int N, int K,
     if (num_cus < 1)
         num_cus = 1;
     const long long cus = num_cus;
+    // A few vectors (2 <= N <= 8) against a matrix contiguous in k, over a K
+    // deep enough for the threads of a workgroup to share: the same kernel
+    // with every 4-float chunk of A meeting the vectors' four k. Every
+    // workgroup reads all the vectors, so it pays where they are few and
+    // contiguous (B transposed, N <= 4: 16384 x 2 x 4096 38 against 44 µs)
+    // or where the 64 x 32 tiles would not fill the CUs (4096 x 8 x 4096:
+    // 27 against 34 µs); on a full grid of those tiles with B stored K x N or
+    // eight vectors the tiles win (16384 x 8 x 4096: 45 against 106 µs).
+    if (N >= 2 && N <= 8 && transA == 0 && K >= 512 &&
+        ((transB == 1 && N <= 4) || ceil_div(M, 64) * batch < cus))
+        return SGEMM_VARIANT_GEMV;
     const long long tiles64 = ceil_div(M, 64) * ceil_div(N, 64) * batch;
     const long long tiles32 = ceil_div(M, 32) * ceil_div(N, 64) * batch;
     const long long tiles6432 = ceil_div(M, 64) * ceil_div(N, 32) * batch;
@@ -1688,7 +1804,8 @@ int launch(const Call &c, int variant, hipStream_t s, Split sk = Split{nullptr, 
 }
 
 // The GEMV kernels over every batch item of an N == 1 call whose op(B) is
-// contiguous in k: op(A) contiguous in k (transA == 0) or along M.
+// contiguous in k (op(A) contiguous in k, transA == 0, or along M), or of a
+// call with 2 <= N <= 8 and op(A) contiguous in k (op(B) either way).
 int launch_gemv(const Call &c, hipStream_t s)
 {
     int cus = 0;
@@ -1698,7 +1815,22 @@ int launch_gemv(const Call &c, hipStream_t s)
     long long blocks;
     int threads;
     KernelFn fn;
-    if (c.tA == 0) {
+    if (c.N > 1) {
+        // A few vectors (2 <= N <= 8, A contiguous in k): four rows per
+        // workgroup, or one on small grids, as for one vector.
+        const bool four = ceil_div(c.M, 4) * c.batch >= 2LL * cus;
+        const int nv = c.N <= 2 ? 2 : c.N <= 4 ? 4 : 8;
+        static const KernelFn kc[2][3] = {
+            {sgemv_nv_kernel<1, 2, true>, sgemv_nv_kernel<1, 4, true>, sgemv_nv_kernel<1, 8, true>},
+            {sgemv_nv_kernel<4, 2, true>, sgemv_nv_kernel<4, 4, true>, sgemv_nv_kernel<4, 8, true>}};
+        static const KernelFn kn[2][2] = {
+            {sgemv_nv_kernel<1, 4, false>, sgemv_nv_kernel<1, 8, false>},
+            {sgemv_nv_kernel<4, 4, false>, sgemv_nv_kernel<4, 8, false>}};
+        // (B stored K x N: the host guarantees N % 4 == 0, so nv == N.)
+        fn = c.tB == 1 ? kc[four][nv == 2 ? 0 : nv == 4 ? 1 : 2] : kn[four][nv == 4 ? 0 : 1];
+        blocks = ceil_div(c.M, four ? 4 : 1);
+        threads = 256;
+    } else if (c.tA == 0) {
         // Four rows per workgroup, or one when that leaves fewer than two
         // workgroups per CU.
         const int rows = ceil_div(c.M, 4) * c.batch >= 2LL * cus ? 4 : 1;
@@ -1727,7 +1859,7 @@ int launch_gemv(const Call &c, hipStream_t s)
     p.Barr = c.Barr;
     p.Carr = c.Carr;
     p.M = c.M;
-    p.N = 1;
+    p.N = c.N;
     p.K = c.K;
     p.lda = c.lda;
     p.ldb = c.ldb;
@@ -1790,11 +1922,15 @@ int launch_canonical(const Call &c, int variant, hipStream_t s, Split sk)
         return -18;
     }
     if (variant == SGEMM_VARIANT_GEMV) {
-        if (!((c.N == 1 && c.tB == 1) || (c.M == 1 && c.tA == 0)))
+        const bool direct = (c.N == 1 && c.tB == 1) || (c.N >= 2 && c.N <= 8 && c.tA == 0);
+        // (A few rows, 2 <= M <= 8, would need C^T written with a column
+        // stride; those stay with the tiles.)
+        const bool mirror = c.M == 1 && c.tA == 0;
+        if (!direct && !mirror)
             return -18;
         if (sk.splits >= 2)
             return -19;
-        if (c.N == 1 && c.tB == 1)
+        if (direct)
             return launch_gemv(c, s);
         // M == 1: the transpose, C^T (N x 1, rows 1 apart) = op(B)^T op(A)^T,
         // whose matrix is op(B)^T (B with the other transpose flag) and whose

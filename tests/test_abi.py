@@ -155,7 +155,18 @@ def test_select_variant(pg):
         assert sel(tA, tB, 16384, 1, 4096, 1, True, 256) != pg.VARIANT_GEMV
     for tA, tB in ((1, 0), (1, 1)):
         assert sel(tA, tB, 1, 16384, 4096, 1, True, 256) != pg.VARIANT_GEMV
-    assert sel(0, 1, 16384, 2, 4096, 1, True, 256) != pg.VARIANT_GEMV
+    # a few vectors (2 <= N <= 8) against a matrix contiguous in k, K >= 512:
+    # up to four contiguous ones on any grid, otherwise only where the 64 x 32
+    # tiles would not fill the CUs (4096 rows: 64 tiles)
+    for tB in (0, 1):
+        for n in (2, 3, 5, 8):
+            assert sel(0, tB, 4096, n, 4096, 1, True, 256) == pg.VARIANT_GEMV, (tB, n)
+            want = tB == 1 and n <= 4
+            assert (sel(0, tB, 16384, n, 4096, 1, True, 256) == pg.VARIANT_GEMV) == want
+        assert sel(0, tB, 4096, 8, 256, 1, True, 256) != pg.VARIANT_GEMV
+    assert sel(1, 1, 16384, 2, 4096, 1, True, 256) != pg.VARIANT_GEMV
+    assert sel(0, 1, 16384, 9, 4096, 1, True, 256) != pg.VARIANT_GEMV
+    assert sel(1, 1, 4, 16384, 4096, 1, True, 256) != pg.VARIANT_GEMV
     # N <= 32 < M: the 64 x 32 tile for small grids or any grid over K >= 512;
     # M <= 32 with K >= 512: the 32 x 64 tile on any grid
     for shape in ((16384, 1, 4096), (65536, 32, 4096), (4096, 8, 256), (100, 32, 64)):
@@ -310,7 +321,9 @@ def test_select_variant_is_always_a_kernel(pg, tA, tB, M, N, K, batch, vec4, cus
     few6432 = -(-M // 64) * -(-N // 32) * batch <= cus
     t6432 = M > 32 and (few6432 or K >= 512 if N <= 32 else few6432 and K >= 512)
     t3264 = -(-M // 32) * -(-N // 64) * batch <= cus or (M <= 32 and K >= 512)
-    gemv = (N == 1 and tB == 1) or (M == 1 and tA == 0)
+    gemv = (N == 1 and tB == 1) or (M == 1 and tA == 0) or \
+        (2 <= N <= 8 and tA == 0 and K >= 512 and
+         ((tB == 1 and N <= 4) or -(-M // 64) * batch < cus))
     if vec4 and gemv:
         assert v == pg.VARIANT_GEMV
     elif vec4 and t6432:

@@ -643,7 +643,7 @@ def test_vector_operand_descriptions_agree(env, M, N, K):
 
 def gemv_cases():
     """(name, tA, tB, M, N, K, lda, ldb, ldc, batch) for the GEMV kernels: N == 1
-    and its mirror M == 1; the matrix contiguous in k (any row count) or along
+    and its mirror M == 1; 2 <= N <= 8 with the matrix contiguous in k; the matrix contiguous in k (any row count) or along
     the outputs (counts that are multiples of 4); the vector in the
     k-contiguous description and in the stride-1 description the library
     converts; counts on both sides of each kernel's workgroup-size choice; K
@@ -668,6 +668,16 @@ def gemv_cases():
     out.append(("m1t_64", 0, 0, 1, 4096, 132, 132, 4100, 4096, 4))
     out.append(("n1t_32", 1, 1, 8192, 1, 36, 8192, 36, 2, 1))
     out.append(("m1t_32", 0, 0, 1, 2048, 100, 100, 2052, 2048, 4))
+    # a few vectors against a matrix contiguous in k: B's rows (any N up to 8)
+    # or B stored K x N (N a multiple of 4)
+    for L in (1, 3, 257, 4099):
+        for N in (2, 3, 4, 5, 8):
+            for K in (4, 1028):
+                if L * K > 5_000_000:
+                    continue
+                out.append((f"nv{N}_{L}x{K}", 0, 1, L, N, K, K + 4 * (L % 2), K, N + L % 3, 1))
+                if N % 4 == 0:
+                    out.append((f"nv{N}n_{L}x{K}", 0, 0, L, N, K, K, N + 4 * (L % 2), N, 2))
     for L, K in ((300, 1028), (1000, 260)):
         out.append((f"n1_vec_{L}x{K}", 0, 0, L, 1, K, K, 1, 1, 3))
         out.append((f"m1_vec_{L}x{K}", 1, 1, 1, L, K, 1, K + 4, L, 3))
@@ -694,7 +704,9 @@ def test_gemv_bitwise(env, variant):
 @pytest.mark.parametrize("tA,tB,M,N,K", [(0, 1, 16384, 1, 4096), (0, 1, 4096, 1, 4096),
                                          (0, 1, 1, 16384, 4096), (0, 1, 1024, 1, 65536),
                                          (1, 1, 16384, 1, 4096), (1, 1, 4096, 1, 4096),
-                                         (0, 0, 1, 16384, 4096), (1, 1, 1024, 1, 65536)])
+                                         (0, 0, 1, 16384, 4096), (1, 1, 1024, 1, 65536),
+                                         (0, 1, 16384, 3, 4096), (0, 0, 4096, 8, 4096),
+                                         (0, 1, 512, 8, 65536)])
 def test_gemv_float_at_size(env, tA, tB, M, N, K):
     """U(-1, 1) inputs at the sizes the kernels are for, checked against the
     oracle's bound on rows from both ends (for M == 1, the whole row)."""
@@ -716,8 +728,8 @@ def test_gemv_refuses_other_calls(env):
     """Forced on a call it does not cover, the GEMV variant returns -18, and
     it never splits K (-19)."""
     _, pg = env
-    for tA, tB, M, N, K in ((0, 0, 64, 64, 64), (0, 1, 64, 2, 64), (1, 0, 2, 64, 64),
-                            (0, 0, 64, 1, 64)):
+    for tA, tB, M, N, K in ((0, 0, 64, 64, 64), (0, 1, 64, 9, 64), (1, 0, 2, 64, 64),
+                            (0, 0, 64, 1, 64), (1, 1, 64, 2, 64), (0, 1, 4, 64, 64)):
         w = Workload("gemv_no", tA, tB, M, N, K, 1.0, 0.0, seed=1,
                      ldb=(K if tB else N) + (8 if (tA, tB, N) == (0, 0, 1) else 0))
         A, B, C = workloads.make_inputs(w)
