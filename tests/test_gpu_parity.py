@@ -822,12 +822,15 @@ def test_pointer_array_bitwise(env, variant):
 
 
 def test_pointer_array_gemv(env):
-    """Pointer-array batches through the GEMV kernel (N == 1 and M == 1):
-    items off 16-byte alignment take its plain path; all exact."""
+    """Pointer-array batches through the GEMV kernels (N == 1, M == 1 and a
+    few vectors): items off 16-byte alignment take their plain paths; all
+    exact."""
     for tA, tB, M, N, K, lda, ldb, ldc in ((0, 1, 300, 1, 132, 136, 132, 2),
                                            (0, 1, 1, 260, 68, 68, 72, 260),
                                            (1, 1, 300, 1, 132, 304, 132, 2),
-                                           (0, 0, 1, 260, 68, 68, 264, 260)):
+                                           (0, 0, 1, 260, 68, 68, 264, 260),
+                                           (0, 1, 300, 3, 132, 136, 140, 5),
+                                           (0, 0, 300, 8, 132, 132, 12, 8)):
         st, res = run_pointer_array(env, tA, tB, M, N, K, 1.5, -0.5, lda, ldb, ldc, batch=5,
                                     seed=41 + M, dist="int3", misalign=(1, 3), shared_a=(4,),
                                     variant=pg_constants.VARIANT_GEMV)
