@@ -123,7 +123,8 @@ enum sgemm_variant {
                                     transB == 1, or M == 1 with transA == 0 (the vector
                                     contiguous in k), the matrix either way; or a few
                                     vectors, 2 <= N <= 8, with transA == 0 (B either
-                                    way); -18 for any other call */
+                                    way), or a few rows, 2 <= M <= 8, with transB == 1
+                                    (A either way); -18 for any other call */
     SGEMM_VARIANT_COUNT = 11
 };
 

@@ -1227,11 +1227,12 @@ __global__ void __launch_bounds__(256) sgemv_kernel(Params p)
 }
 
 // The same for a few vectors, 2 <= N <= NV: y[m, j] = alpha * sum_k A[m, k]
-// op(B)[k, j] + beta * y[m, j], y[m, j] at C[m * ldc + j]. op(B) is B's rows
-// (B_KC: B stored N x K, vector j at B + j * ldb) or B stored K x N (rows of N
-// floats ldb apart; N is then a multiple of 4 and NV == N). Each thread's
-// 4-float chunk of k of every row meets the same four k of every vector.
-template <int ROWS, int NV, bool B_KC>
+// op(B)[k, j] + beta * y[m, j], y[m, j] at C[m * ldc + j] (CT: at
+// C[j * ldc + m], the product written transposed). op(B) is B's rows (B_KC: B
+// stored N x K, vector j at B + j * ldb) or B stored K x N (rows of N floats
+// ldb apart; N is then a multiple of 4 and NV == N). Each thread's 4-float
+// chunk of k of every row meets the same four k of every vector.
+template <int ROWS, int NV, bool B_KC, bool CT>
 __global__ void __launch_bounds__(256) sgemv_nv_kernel(Params p)
 {
     constexpr int T = 256, WAVES = T / 64;
@@ -1325,7 +1326,7 @@ __global__ void __launch_bounds__(256) sgemv_nv_kernel(Params p)
 #pragma unroll
             for (int w = 1; w < WAVES; ++w)
                 sum += part[w][r][j];
-            float *y = C + (long long)(m0 + r) * p.ldc + j;
+            float *y = CT ? C + (long long)j * p.ldc + (m0 + r) : C + (long long)(m0 + r) * p.ldc + j;
             *y = p.beta == 0.0f ? p.alpha * sum : p.alpha * sum + p.beta * *y;
         }
     }
@@ -1619,6 +1620,12 @@ extern "C" int sgemm_select_variant(int transA, int transB, int M, int N, int K,
     if (N >= 2 && N <= 8 && transA == 0 && K >= 512 &&
         ((transB == 1 && N <= 4) || ceil_div(M, 64) * batch < cus))
         return SGEMM_VARIANT_GEMV;
+    // The mirror: a few rows (2 <= M <= 8) against B stored N x K, run as the
+    // transpose with C^T written transposed (Y = X W^T with X a handful of
+    // rows and W stored N x K).
+    if (M >= 2 && M <= 8 && transB == 1 && K >= 512 &&
+        ((transA == 0 && M <= 4) || ceil_div(N, 64) * batch < cus))
+        return SGEMM_VARIANT_GEMV;
     const long long tiles64 = ceil_div(M, 64) * ceil_div(N, 64) * batch;
     const long long tiles32 = ceil_div(M, 32) * ceil_div(N, 64) * batch;
     const long long tiles6432 = ceil_div(M, 64) * ceil_div(N, 32) * batch;
@@ -1805,8 +1812,9 @@ int launch(const Call &c, int variant, hipStream_t s, Split sk = Split{nullptr, 
 
 // The GEMV kernels over every batch item of an N == 1 call whose op(B) is
 // contiguous in k (op(A) contiguous in k, transA == 0, or along M), or of a
-// call with 2 <= N <= 8 and op(A) contiguous in k (op(B) either way).
-int launch_gemv(const Call &c, hipStream_t s)
+// call with 2 <= N <= 8 and op(A) contiguous in k (op(B) either way);
+// c_transposed: the product goes to C transposed (C^T of the caller's call).
+int launch_gemv(const Call &c, hipStream_t s, bool c_transposed)
 {
     int cus = 0;
     const int st = num_cus_of_current_device(&cus);
@@ -1820,14 +1828,23 @@ int launch_gemv(const Call &c, hipStream_t s)
         // workgroup, or one on small grids, as for one vector.
         const bool four = ceil_div(c.M, 4) * c.batch >= 2LL * cus;
         const int nv = c.N <= 2 ? 2 : c.N <= 4 ? 4 : 8;
-        static const KernelFn kc[2][3] = {
-            {sgemv_nv_kernel<1, 2, true>, sgemv_nv_kernel<1, 4, true>, sgemv_nv_kernel<1, 8, true>},
-            {sgemv_nv_kernel<4, 2, true>, sgemv_nv_kernel<4, 4, true>, sgemv_nv_kernel<4, 8, true>}};
-        static const KernelFn kn[2][2] = {
-            {sgemv_nv_kernel<1, 4, false>, sgemv_nv_kernel<1, 8, false>},
-            {sgemv_nv_kernel<4, 4, false>, sgemv_nv_kernel<4, 8, false>}};
+        static const KernelFn kc[2][2][3] = {
+            {{sgemv_nv_kernel<1, 2, true, false>, sgemv_nv_kernel<1, 4, true, false>,
+              sgemv_nv_kernel<1, 8, true, false>},
+             {sgemv_nv_kernel<4, 2, true, false>, sgemv_nv_kernel<4, 4, true, false>,
+              sgemv_nv_kernel<4, 8, true, false>}},
+            {{sgemv_nv_kernel<1, 2, true, true>, sgemv_nv_kernel<1, 4, true, true>,
+              sgemv_nv_kernel<1, 8, true, true>},
+             {sgemv_nv_kernel<4, 2, true, true>, sgemv_nv_kernel<4, 4, true, true>,
+              sgemv_nv_kernel<4, 8, true, true>}}};
+        static const KernelFn kn[2][2][2] = {
+            {{sgemv_nv_kernel<1, 4, false, false>, sgemv_nv_kernel<1, 8, false, false>},
+             {sgemv_nv_kernel<4, 4, false, false>, sgemv_nv_kernel<4, 8, false, false>}},
+            {{sgemv_nv_kernel<1, 4, false, true>, sgemv_nv_kernel<1, 8, false, true>},
+             {sgemv_nv_kernel<4, 4, false, true>, sgemv_nv_kernel<4, 8, false, true>}}};
         // (B stored K x N: the host guarantees N % 4 == 0, so nv == N.)
-        fn = c.tB == 1 ? kc[four][nv == 2 ? 0 : nv == 4 ? 1 : 2] : kn[four][nv == 4 ? 0 : 1];
+        fn = c.tB == 1 ? kc[c_transposed][four][nv == 2 ? 0 : nv == 4 ? 1 : 2]
+                       : kn[c_transposed][four][nv == 4 ? 0 : 1];
         blocks = ceil_div(c.M, four ? 4 : 1);
         threads = 256;
     } else if (c.tA == 0) {
@@ -1923,23 +1940,21 @@ int launch_canonical(const Call &c, int variant, hipStream_t s, Split sk)
     }
     if (variant == SGEMM_VARIANT_GEMV) {
         const bool direct = (c.N == 1 && c.tB == 1) || (c.N >= 2 && c.N <= 8 && c.tA == 0);
-        // (A few rows, 2 <= M <= 8, would need C^T written with a column
-        // stride; those stay with the tiles.)
-        const bool mirror = c.M == 1 && c.tA == 0;
+        const bool mirror = (c.M == 1 && c.tA == 0) || (c.M >= 2 && c.M <= 8 && c.tB == 1);
         if (!direct && !mirror)
             return -18;
         if (sk.splits >= 2)
             return -19;
         if (direct)
-            return launch_gemv(c, s);
-        // M == 1: the transpose, C^T (N x 1, rows 1 apart) = op(B)^T op(A)^T,
-        // whose matrix is op(B)^T (B with the other transpose flag) and whose
-        // vector is A's row.
+            return launch_gemv(c, s, false);
+        // M <= 8: the transpose, C^T = op(B)^T op(A)^T, whose matrix is op(B)^T
+        // (B with the other transpose flag) and whose vectors are op(A)'s rows;
+        // C^T is N x 1 with rows 1 apart for M == 1, else written transposed.
         Call t = c;
         t.M = c.N;
-        t.N = 1;
+        t.N = c.M;
         t.tA = 1 - c.tB;
-        t.tB = 1;
+        t.tB = 1 - c.tA;
         t.A = c.B;
         t.B = c.A;
         t.Aarr = c.Barr;
@@ -1948,8 +1963,8 @@ int launch_canonical(const Call &c, int variant, hipStream_t s, Split sk)
         t.ldb = c.lda;
         t.sA = c.sB;
         t.sB = c.sA;
-        t.ldc = 1;
-        return launch_gemv(t, s);
+        t.ldc = c.M == 1 ? 1 : c.ldc;
+        return launch_gemv(t, s, c.M > 1);
     }
 
     // Split-K: the tile kernels write per-slice partial tiles into the

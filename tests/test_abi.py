@@ -166,7 +166,14 @@ def test_select_variant(pg):
         assert sel(0, tB, 4096, 8, 256, 1, True, 256) != pg.VARIANT_GEMV
     assert sel(1, 1, 16384, 2, 4096, 1, True, 256) != pg.VARIANT_GEMV
     assert sel(0, 1, 16384, 9, 4096, 1, True, 256) != pg.VARIANT_GEMV
-    assert sel(1, 1, 4, 16384, 4096, 1, True, 256) != pg.VARIANT_GEMV
+    # the mirror: a few rows against B stored N x K
+    for tA in (0, 1):
+        for m in (2, 3, 5, 8):
+            assert sel(tA, 1, m, 4096, 4096, 1, True, 256) == pg.VARIANT_GEMV, (tA, m)
+            want = tA == 0 and m <= 4
+            assert (sel(tA, 1, m, 16384, 4096, 1, True, 256) == pg.VARIANT_GEMV) == want
+    assert sel(0, 0, 4, 4096, 4096, 1, True, 256) != pg.VARIANT_GEMV
+    assert sel(0, 1, 4, 4096, 256, 1, True, 256) != pg.VARIANT_GEMV
     # N <= 32 < M: the 64 x 32 tile for small grids or any grid over K >= 512;
     # M <= 32 with K >= 512: the 32 x 64 tile on any grid
     for shape in ((16384, 1, 4096), (65536, 32, 4096), (4096, 8, 256), (100, 32, 64)):
@@ -323,7 +330,9 @@ def test_select_variant_is_always_a_kernel(pg, tA, tB, M, N, K, batch, vec4, cus
     t3264 = -(-M // 32) * -(-N // 64) * batch <= cus or (M <= 32 and K >= 512)
     gemv = (N == 1 and tB == 1) or (M == 1 and tA == 0) or \
         (2 <= N <= 8 and tA == 0 and K >= 512 and
-         ((tB == 1 and N <= 4) or -(-M // 64) * batch < cus))
+         ((tB == 1 and N <= 4) or -(-M // 64) * batch < cus)) or \
+        (2 <= M <= 8 and tB == 1 and K >= 512 and
+         ((tA == 0 and M <= 4) or -(-N // 64) * batch < cus))
     if vec4 and gemv:
         assert v == pg.VARIANT_GEMV
     elif vec4 and t6432:

@@ -643,7 +643,8 @@ def test_vector_operand_descriptions_agree(env, M, N, K):
 
 def gemv_cases():
     """(name, tA, tB, M, N, K, lda, ldb, ldc, batch) for the GEMV kernels: N == 1
-    and its mirror M == 1; 2 <= N <= 8 with the matrix contiguous in k; the matrix contiguous in k (any row count) or along
+    and its mirror M == 1; 2 <= N <= 8 with the matrix contiguous in k and its
+    mirror 2 <= M <= 8; the matrix contiguous in k (any row count) or along
     the outputs (counts that are multiples of 4); the vector in the
     k-contiguous description and in the stride-1 description the library
     converts; counts on both sides of each kernel's workgroup-size choice; K
@@ -678,6 +679,11 @@ def gemv_cases():
                 out.append((f"nv{N}_{L}x{K}", 0, 1, L, N, K, K + 4 * (L % 2), K, N + L % 3, 1))
                 if N % 4 == 0:
                     out.append((f"nv{N}n_{L}x{K}", 0, 0, L, N, K, K, N + 4 * (L % 2), N, 2))
+                # the mirror: N rows of A against B stored L x K, C written
+                # through the transpose
+                out.append((f"mv{N}_{L}x{K}", 0, 1, N, L, K, K + 4 * (L % 2), K + 4, L + L % 3, 1))
+                if N % 4 == 0:
+                    out.append((f"mv{N}t_{L}x{K}", 1, 1, N, L, K, N + 4 * (L % 2), K, L, 2))
     for L, K in ((300, 1028), (1000, 260)):
         out.append((f"n1_vec_{L}x{K}", 0, 0, L, 1, K, K, 1, 1, 3))
         out.append((f"m1_vec_{L}x{K}", 1, 1, 1, L, K, 1, K + 4, L, 3))
@@ -706,17 +712,19 @@ def test_gemv_bitwise(env, variant):
                                          (1, 1, 16384, 1, 4096), (1, 1, 4096, 1, 4096),
                                          (0, 0, 1, 16384, 4096), (1, 1, 1024, 1, 65536),
                                          (0, 1, 16384, 3, 4096), (0, 0, 4096, 8, 4096),
-                                         (0, 1, 512, 8, 65536)])
+                                         (0, 1, 512, 8, 65536), (0, 1, 4, 16384, 4096),
+                                         (1, 1, 8, 4096, 4096)])
 def test_gemv_float_at_size(env, tA, tB, M, N, K):
     """U(-1, 1) inputs at the sizes the kernels are for, checked against the
-    oracle's bound on rows from both ends (for M == 1, the whole row)."""
+    oracle's bound on rows from both ends and the middle (for a few rows, all of
+    them)."""
     _, pg = env
     w = Workload("gemv_f", tA, tB, M, N, K, 1.0, 0.5, seed=M + N + K + tA + tB)
     A, B, C = workloads.make_inputs(w)
     assert pg.sgemm_select_variant(tA, tB, M, N, K, 1, 1, 256) == pg.VARIANT_GEMV
     st, got = run_gpu(env, w, A, B, C)
     assert st == 0
-    if M == 1:
+    if M <= 192:
         check_against_oracle(w, A, B, C, got)
     else:
         for rows in ((0, 64), (M // 2, M // 2 + 64), (M - 64, M)):
@@ -729,7 +737,8 @@ def test_gemv_refuses_other_calls(env):
     it never splits K (-19)."""
     _, pg = env
     for tA, tB, M, N, K in ((0, 0, 64, 64, 64), (0, 1, 64, 9, 64), (1, 0, 2, 64, 64),
-                            (0, 0, 64, 1, 64), (1, 1, 64, 2, 64), (0, 1, 4, 64, 64)):
+                            (0, 0, 64, 1, 64), (1, 1, 64, 2, 64), (0, 0, 4, 64, 64),
+                            (0, 1, 9, 64, 64)):
         w = Workload("gemv_no", tA, tB, M, N, K, 1.0, 0.0, seed=1,
                      ldb=(K if tB else N) + (8 if (tA, tB, N) == (0, 0, 1) else 0))
         A, B, C = workloads.make_inputs(w)
