@@ -732,6 +732,50 @@ def test_gemv_float_at_size(env, tA, tB, M, N, K):
     check_untouched(w, C, got)
 
 
+def test_gemv_random_shapes(env):
+    """80 seeded matrix-vector shapes through the automatic dispatch: one of M,
+    N from 1 to 8 and the other up to 2000, K up to 2052, every transpose
+    pair, padded leading dimensions, batches, integer inputs: bitwise equal to
+    the oracle, nothing outside C's windows touched. Most reach a GEMV kernel
+    (the one-vector, few-vector, mirror and output-contiguous paths); the
+    rest check that the shapes the GEMV kernels leave alone still run."""
+    _, pg = env
+    rng = np.random.default_rng(2024)
+    cus = 256
+    reached = 0
+    for i in range(80):
+        small = int(rng.choice([1, 1, 2, 3, 4, 4, 5, 8]))
+        big = int(rng.integers(1, 2000))
+        K = int(rng.choice([4, 36, 516, 1028, 2052]))
+        if rng.random() < 0.9:
+            big = max(4, big // 4 * 4)
+        rows_small = rng.random() < 0.5
+        M, N = (small, big) if rows_small else (big, small)
+        # mostly the layouts the GEMV kernels take, some others
+        lean = int(rng.random() < 0.75)
+        if rows_small:
+            tA, tB = int(rng.integers(0, 2)), lean if rng.random() < 0.9 else 1 - lean
+        else:
+            tA, tB = 1 - lean if rng.random() < 0.9 else lean, int(rng.integers(0, 2))
+        pad = lambda: int(rng.choice([0, 0, 4, 8]))
+        batch = int(rng.choice([1, 1, 2, 3]))
+        alpha, beta = (1.0, 0.0) if i % 3 == 0 else ((-2.0, 0.5) if i % 3 == 1 else (0.5, -1.0))
+        w = Workload(f"grnd{i}", tA, tB, M, N, K, alpha, beta, seed=3000 + i, dist="int3",
+                     batch=batch, lda=(M if tA else K) + pad(), ldb=(K if tB else N) + pad(),
+                     ldc=N + pad())
+        A, B, C = workloads.make_inputs(w)
+        cA, cB, _, _ = canonical_vectors(tA, tB, M, N, K, w.LDA, w.LDB)
+        v = pg.sgemm_select_variant(cA, cB, M, N, K, batch, 1 if vec4_possible(w) else 0, cus)
+        reached += v == pg.VARIANT_GEMV
+        log(f"[gemv-random] {w.name} {'NT'[tA]}{'NT'[tB]} {M}x{N}x{K} b{batch} "
+            f"ld {w.LDA},{w.LDB},{w.LDC} -> {pg.VARIANT_NAMES[v]}")
+        st, got = run_gpu(env, w, A, B, C)
+        assert st == 0, (w, st)
+        check_against_oracle(w, A, B, C, got, exact=True)
+        check_untouched(w, C, got)
+    assert reached >= 30, reached
+
+
 def test_gemv_refuses_other_calls(env):
     """Forced on a call it does not cover, the GEMV variant returns -18, and
     it never splits K (-19)."""
