@@ -1855,16 +1855,24 @@ int launch_gemv(const Call &c, hipStream_t s, bool c_transposed)
         threads = 256;
         fn = rows == 4 ? sgemv_kernel<4> : sgemv_kernel<1>;
     } else {
-        // The widest block of outputs (64, 32 or 16: row segments of 256, 128
-        // or 64 bytes) that still gives every CU a workgroup, else 16
+        // The widest block of outputs (64, 32, 16 or 8: row segments of 256,
+        // 128, 64 or 32 bytes) that still gives every CU a workgroup
         // (16384 x 1 x 4096: 38 µs with 64, 44 with 32, 50 with 16; 8192 x 1 x
-        // 8192: 42, 40, 48 µs; 4096 x 1 x 4096: 20, 15, 14 µs).
-        const int bc = ceil_div(c.M, 64) * c.batch >= cus   ? 64
-                       : ceil_div(c.M, 32) * c.batch >= cus ? 32
-                                                            : 16;
+        // 8192: 42, 40, 48 µs; 4096 x 1 x 4096: 20, 15, 14 µs; 2048 x 1 x
+        // 16384: 35 µs with 16, 32 with 8). Below that 8, or 4 (16-byte
+        // segments) over K >= 16384, where a deep K leaves the few workgroups
+        // the whole call (1024 x 1 x 65536: 131, 109, 96 µs with 16, 8, 4;
+        // 512 x 1 x 8192: 6.9 µs with 8, 8.2 with 4).
+        const int bc = ceil_div(c.M, 64) * c.batch >= cus                    ? 64
+                       : ceil_div(c.M, 32) * c.batch >= cus                  ? 32
+                       : ceil_div(c.M, 16) * c.batch >= cus                  ? 16
+                       : ceil_div(c.M, 8) * c.batch >= cus || c.K < 16384 ? 8
+                                                                             : 4;
         blocks = ceil_div(c.M, bc);
         threads = 512;
-        fn = bc == 64 ? sgemv_t_kernel<64> : bc == 32 ? sgemv_t_kernel<32> : sgemv_t_kernel<16>;
+        static const KernelFn kt[5] = {sgemv_t_kernel<4>, sgemv_t_kernel<8>, sgemv_t_kernel<16>,
+                                       sgemv_t_kernel<32>, sgemv_t_kernel<64>};
+        fn = kt[bc == 4 ? 0 : bc == 8 ? 1 : bc == 16 ? 2 : bc == 32 ? 3 : 4];
     }
     if (blocks * threads > INT32_MAX)
         return -22;

@@ -668,6 +668,10 @@ def gemv_cases():
     out.append(("n1t_64", 1, 1, 16384, 1, 68, 16388, 68, 1, 1))
     out.append(("m1t_64", 0, 0, 1, 4096, 132, 132, 4100, 4096, 4))
     out.append(("n1t_32", 1, 1, 8192, 1, 36, 8192, 36, 2, 1))
+    # the 8- and 4-wide blocks: few outputs, the latter over K >= 16384
+    out.append(("n1t_8", 1, 1, 1000, 1, 1100, 1004, 1100, 1, 1))
+    out.append(("n1t_4", 1, 1, 64, 1, 16388, 68, 16388, 1, 1))
+    out.append(("m1t_4", 0, 0, 1, 128, 16384, 16384, 132, 128, 2))
     out.append(("m1t_32", 0, 0, 1, 2048, 100, 100, 2052, 2048, 4))
     # a few vectors against a matrix contiguous in k: B's rows (any N up to 8)
     # or B stored K x N (N a multiple of 4)
