@@ -128,14 +128,18 @@ def sweep(shapes, rounds: int = 3, target_ms: float = 20.0, out=sys.stdout):
         lda, ldb = A.shape[2], B.shape[2]
         sa, sb, sc = A.stride(0), B.stride(0), C.stride(0)
         # The library first describes a stride-1 vector operand as contiguous
-        # in k; its choice, and whether the GEMV kernels (N == 1 or M == 1 with
-        # the vector contiguous in k) take the call, follow that description.
+        # in k; its choice, and whether the GEMV kernels take the call (N == 1
+        # or M == 1 with the vector contiguous in k; a few vectors, 2 to 8,
+        # against a matrix contiguous in k, or the mirror), follow that
+        # description.
         cA, cB = tA, tB
         if N == 1 and tB == 0 and ldb == 1 and 1 < K < 1 << 21:
             cB = 1
         if M == 1 and tA == 1 and lda == 1 and 1 < K < 1 << 21:
             cA = 0
-        gemv_ok = (N == 1 and cB == 1) or (M == 1 and cA == 0)
+        gemv_ok = ((N == 1 and cB == 1) or (M == 1 and cA == 0) or
+                   (2 <= N <= 8 and cA == 0 and (cB == 1 or N % 4 == 0)) or
+                   (2 <= M <= 8 and cB == 1 and (cA == 0 or M % 4 == 0)))
         auto = pg.sgemm_select_variant(cA, cB, M, N, K, batch, 1, cus)
         variants = [v for v in range(pg.VARIANT_COUNT) if v != pg.VARIANT_S64x64_V1 and
                     (v != pg.VARIANT_GEMV or gemv_ok)]
