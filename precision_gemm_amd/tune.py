@@ -71,6 +71,8 @@ WIDE_SHAPES = [
     (0, 0, 16384, 1, 4096, 1, 0.0), (0, 0, 16384, 16, 4096, 1, 0.0),
     (0, 1, 65536, 32, 4096, 1, 0.0), (0, 0, 32, 16384, 4096, 1, 0.0),
     (1, 0, 8, 65536, 2048, 1, 0.0), (0, 0, 4096, 24, 1024, 4, 0.0),
+    (0, 1, 16384, 4, 4096, 1, 0.0), (0, 0, 4096, 8, 4096, 1, 0.0),
+    (0, 1, 4, 16384, 4096, 1, 0.0), (0, 1, 8, 16384, 4096, 1, 0.0),
 ]
 
 # Mid-size grids over deep K (one to five rounds of tiles), where the 64 x 32
