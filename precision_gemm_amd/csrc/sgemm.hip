@@ -1267,7 +1267,7 @@ __global__ void __launch_bounds__(256) sgemv_nv_kernel(Params p)
             }
         }
     } else {
-        const int K4 = p.K >> 2; // the host guarantees K % 4 == 0 and lda % 4 == 0
+        const int K4 = p.K >> 2; // the host guarantees K, lda and ldb % 4 == 0
 #pragma unroll 2
         for (int c = t; c < K4; c += T) {
             float x[4][NV];
