@@ -386,14 +386,17 @@ def test_deterministic(env):
 def test_concurrent_host_threads(env):
     """Calls from several host threads at once, each on a stream of its own
     (the library keeps no per-call state; the CU-count cache is atomic),
-    give the bits of the same calls made one at a time."""
+    give the bits of the same calls made one at a time: tile kernels, split-K
+    with a workspace, a GEMV and a few-row GEMV written transposed."""
     import threading
     torch, pg = env
     dev = torch.device("cuda:0")
     cases = [Workload("thr0", 0, 0, 300, 200, 500, 1.0, 0.5, seed=41),
              Workload("thr1", 1, 1, 257, 129, 1040, -1.5, 0.0, seed=42),
              Workload("thr2", 0, 1, 64, 96, 4096, 1.0, 1.0, seed=43, batch=3),
-             Workload("thr3", 1, 0, 640, 320, 96, 0.5, -2.0, seed=44)]
+             Workload("thr3", 1, 0, 640, 320, 96, 0.5, -2.0, seed=44),
+             Workload("thr4", 0, 1, 2000, 1, 1028, 1.0, 0.5, seed=45),
+             Workload("thr5", 0, 1, 4, 4096, 1028, -1.0, 1.0, seed=46)]
 
     def call(w, dA, dB, dC, stream, ws):
         # thr2 splits K across workgroups through its own workspace
@@ -419,7 +422,7 @@ def test_concurrent_host_threads(env):
         want.append(dC.cpu().numpy().view(np.uint32).copy())
         check_against_oracle(w, A, B, C, dC.cpu().numpy())
 
-    log("[threads] 4 host threads x 25 calls")
+    log(f"[threads] {len(cases)} host threads x 25 calls")
     errors = []
 
     def worker(k):
