@@ -1657,7 +1657,7 @@ extern "C" int sgemm_select_variant(int transA, int transB, int M, int N, int K,
     // Otherwise the tile whose busiest CU finishes first: a CU receives
     // ceil(tiles / CUs) tiles, each costing its area over the variant's
     // relative efficiency. The efficiencies are fitted to sweeps of every
-    // variant over 72 shapes (precision_gemm_amd/tune.py): 128 x 128 tiles
+    // variant over 76 shapes (precision_gemm_amd/tune.py): 128 x 128 tiles
     // 1.00; the K-split 64 x 64 tile 0.88, for K >= 768; plain 64 x 64 tiles
     // 0.85, or 1.05 for K <= 512, where a tile's fixed costs (the first loads,
     // the C stores) outweigh its short K loop and the small tiles, more of
