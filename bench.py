@@ -281,7 +281,7 @@ def main(argv=None) -> int:
 
     achieved = flops / (per_launch_ms * 1e-3) / 1e12
     peak = measure.MI355X_FP32_MFMA_PEAK / 1e12
-    roof = measure.roofline(flops, w.algorithmic_bytes(), measure.MI355X_FP32_MFMA_PEAK,
+    roof = measure.place_on_roofline(flops, w.algorithmic_bytes(), measure.MI355X_FP32_MFMA_PEAK,
                             measure.MI355X_HBM_BW)
     out = {
         "metric": METRIC,

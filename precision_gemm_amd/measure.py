@@ -1,10 +1,9 @@
 """Roofline arithmetic for the benchmark report.
 
-The roofline model follows "Custom GPU kernels & Triton", section 2 (roofline
-and arithmetic intensity): intensity is FLOPs per byte moved from HBM, the
-ridge is peak FLOP/s over bandwidth, the attainable rate is the smaller of the
-peak and intensity times bandwidth, and an operation below the ridge is
-memory-bound.
+The roofline model is the one "Custom GPU kernels & Triton" sets out in
+section 2 (roofline and arithmetic intensity): a kernel is limited either by
+its arithmetic or by the bytes it moves from HBM, its intensity (FLOPs per HBM
+byte) says which, and the ridge is the intensity at which the two limits meet.
 
 The block-tile intensity BM*BN / (2*(BM+BN)) FLOP per byte of fp32 loaded into
 shared memory is the one "From 1% to 94% of cuBLAS, one kernel at a time"
@@ -26,9 +25,9 @@ MI355X_SCLK = 2.4e9
 
 @dataclass(frozen=True)
 class Roof:
-    intensity: float    # FLOP per byte
-    ridge: float        # FLOP per byte where the bound flips
-    attainable: float   # FLOP/s
+    intensity: float    # FLOP per byte moved from HBM
+    ridge: float        # FLOP per byte at which both floors are equal
+    attainable: float   # FLOP/s the slower of the two resources allows
     bound: str          # "memory-bound" or "compute-bound"
     peak: float         # FLOP/s
 
@@ -37,12 +36,22 @@ class Roof:
         return self.attainable / self.peak
 
 
-def roofline(flops: float, bytes_moved: float, peak_flops: float, bw_bytes_per_s: float) -> Roof:
-    ai = flops / bytes_moved
-    ridge = peak_flops / bw_bytes_per_s
-    attainable = min(peak_flops, ai * bw_bytes_per_s)
-    bound = "memory-bound" if ai < ridge else "compute-bound"
-    return Roof(ai, ridge, attainable, bound, peak_flops)
+def place_on_roofline(flops: float, hbm_bytes: float, peak_flops: float,
+                      hbm_bw: float) -> Roof:
+    """Where a kernel doing `flops` and moving `hbm_bytes` sits on the roofline.
+
+    Each resource sets a floor on the kernel's time: the math at the peak rate
+    and the traffic at the HBM rate. The larger floor is the bound, and the work
+    over that floor is the best rate the kernel can reach. A tie (a kernel on the
+    ridge) counts as compute-bound.
+    """
+    t_math = flops / peak_flops
+    t_hbm = hbm_bytes / hbm_bw
+    limited_by_hbm = t_hbm > t_math
+    return Roof(intensity=flops / hbm_bytes, ridge=peak_flops / hbm_bw,
+                attainable=flops / (t_hbm if limited_by_hbm else t_math),
+                bound="memory-bound" if limited_by_hbm else "compute-bound",
+                peak=peak_flops)
 
 
 def block_tile_intensity(bm: int, bn: int) -> float:

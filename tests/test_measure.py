@@ -22,12 +22,12 @@ def test_page_counts_for_4092():
 def test_roofline_reproduces_printed_lab_output():
     g = read_golden("roofline_p3.txt")
     peak, bw = g["peak_tflops"] * 1e12, g["bw_tbs"] * 1e12
-    soft = measure.roofline(g["softmax_ai"] * 1000.0, 1000.0, peak, bw)
+    soft = measure.place_on_roofline(g["softmax_ai"] * 1000.0, 1000.0, peak, bw)
     assert f"{soft.ridge:.1f}" == f"{g['ridge']:.1f}"
     assert soft.bound == "memory-bound"
     assert f"{soft.attainable / 1e12:.1f}" == f"{g['softmax_attainable_tflops']:.1f}"
     assert f"{soft.frac_of_peak * 100:.1f}" == f"{g['softmax_pct']:.1f}"
-    gemm = measure.roofline(g["gemm_ai"] * 1000.0, 1000.0, peak, bw)
+    gemm = measure.place_on_roofline(g["gemm_ai"] * 1000.0, 1000.0, peak, bw)
     assert gemm.bound == "compute-bound"
     assert f"{gemm.attainable / 1e12:.1f}" == f"{g['gemm_attainable_tflops']:.1f}"
     assert f"{gemm.frac_of_peak * 100:.1f}" == f"{g['gemm_pct']:.1f}"
@@ -39,7 +39,7 @@ def test_roofline_reproduces_printed_lab_output():
 def test_mi355x_workload_rooflines():
     """The five workloads against MI355X FP32-MFMA peak and HBM bandwidth."""
     by = workloads.BY_NAME
-    roofs = {n: measure.roofline(w.flops(), w.algorithmic_bytes(),
+    roofs = {n: measure.place_on_roofline(w.flops(), w.algorithmic_bytes(),
                                  measure.MI355X_FP32_MFMA_PEAK, measure.MI355X_HBM_BW)
              for n, w in by.items()}
     assert roofs["sgemm_4092"].bound == "compute-bound"
@@ -58,7 +58,7 @@ def test_bench_roofline_bound_follows_the_ridge():
     import bench
     peak, bw = measure.MI355X_FP32_MFMA_PEAK, measure.MI355X_HBM_BW
     gemv = workloads.BY_NAME["gemv_16384x1x4096_nt"]
-    roof = measure.roofline(gemv.flops(), gemv.algorithmic_bytes(), peak, bw)
+    roof = measure.place_on_roofline(gemv.flops(), gemv.algorithmic_bytes(), peak, bw)
     assert roof.bound == "memory-bound" and roof.intensity == pytest.approx(0.5, abs=0.01)
     ms = 0.04
     tflops = gemv.flops() / (ms * 1e-3) / 1e12
@@ -67,7 +67,7 @@ def test_bench_roofline_bound_follows_the_ridge():
     assert e["achieved"] == pytest.approx(gemv.algorithmic_bytes() / (ms * 1e-3) / 1e9, rel=1e-3)
     assert e["frac"] == pytest.approx(e["achieved"] / 8000.0, abs=1e-4)
     big = workloads.BY_NAME["sgemm_4092"]
-    roof = measure.roofline(big.flops(), big.algorithmic_bytes(), peak, bw)
+    roof = measure.place_on_roofline(big.flops(), big.algorithmic_bytes(), peak, bw)
     ms = 0.91
     tflops = big.flops() / (ms * 1e-3) / 1e12
     e = bench.roofline_entry(big, roof, tflops, peak / 1e12, ms, 123)

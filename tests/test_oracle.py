@@ -306,6 +306,53 @@ def test_bound_check_accepts_rounding_and_rejects_errors():
     assert not oracle.bound_check(nan, ref, S, C, 1.0, 0.5, K).ok
 
 
+# The acceptance bound at its edge. Each case states the limit worked out by
+# hand from the bound 2e-6 * max(K,1) * (|alpha| S + |beta| |c|) and places the
+# GPU value just inside it (must pass) and just outside it (must fail). A bound
+# that lost its factor K, squared it, dropped max(K, 1), took alpha or beta
+# with its sign, or dropped the |beta||c| term fails at least one of them.
+EDGE = 0.05  # relative distance from the limit on either side
+
+
+def _edge_case(ref, S, c_in, alpha, beta, K, limit):
+    inside = np.array([ref + limit * (1 - EDGE), ref - limit * (1 - EDGE)])
+    outside = np.array([ref + limit * (1 + EDGE), ref - limit * (1 + EDGE)])
+    r, s, c = (np.full(2, v, np.float64) for v in (ref, S, c_in))
+    ok = oracle.bound_check(inside, r, s, c, alpha, beta, K)
+    bad = oracle.bound_check(outside, r, s, c, alpha, beta, K)
+    assert ok.ok, ok
+    assert not bad.ok and bad.n_bad == 2, bad
+
+
+def test_bound_edge_negative_alpha_with_beta():
+    # op(A) = [1, -2, 0.5], op(B) = [2, 1, -4]^T: the product is 2 - 2 - 2 = -2,
+    # S = 2 + 2 + 2 = 6; alpha = -2, beta = 0.5, c = 4 give 4 + 2 = 6 and the
+    # limit 2e-6 * 3 * (2 * 6 + 0.5 * 4) = 8.4e-5.
+    ref, S = call(np.array([[1, -2, 0.5]]), np.array([[2], [1], [-4]]), np.array([[4.0]]),
+                  -2.0, 0.5)
+    assert (ref[0, 0], S[0, 0]) == (6.0, 6.0)
+    _edge_case(6.0, 6.0, 4.0, -2.0, 0.5, 3, 8.4e-5)
+
+
+def test_bound_edge_k_zero_uses_max_k_1():
+    # K = 0: C = beta * c = 2 * 3 = 6, S = 0, limit 2e-6 * 1 * (2 * 3) = 1.2e-5
+    # (a bound scaled by K itself would be 0 and reject even the inside case).
+    _edge_case(6.0, 0.0, 3.0, 1.0, 2.0, 0, 1.2e-5)
+
+
+def test_bound_edge_beta_term_dominates():
+    # alpha = 1, S = 1e-3, beta = -4, c = 100, K = 2:
+    # limit 2e-6 * 2 * (1e-3 + 400) = 1.600004e-3, the |beta||c| term nearly all of it.
+    _edge_case(-399.5, 1e-3, 100.0, 1.0, -4.0, 2, 1.600004e-3)
+
+
+def test_bound_edge_scales_with_k():
+    # The same element at K = 1 and K = 1000: S = 2, alpha = 1, beta = 0
+    # (c is not part of the bound): limits 4e-6 and 4e-3.
+    _edge_case(1.0, 2.0, 7.0, 1.0, 0.0, 1, 4e-6)
+    _edge_case(1.0, 2.0, 7.0, 1.0, 0.0, 1000, 4e-3)
+
+
 # ---------------------------------------------------------------- pins vs mutants
 
 def _mutants():
