@@ -13,9 +13,16 @@ Every step is one kernel launch, so the timed region over K is also the
 average launch duration used for the roofline figure.
 
 After the timed region one more launch on the pristine inputs must reproduce
-the first launch's output bit for bit (``determinism``), and ``cold`` times
-single launches after restoring C and flushing L2 and the Infinity Cache with a
-1 GiB fill (median and min; a supplement, not the headline).
+the first launch's output bit for bit (``determinism``). ``hbm_resident`` then
+times the same call on several copies of A, B and C, used in turn, more than
+1 GiB in all: every launch reads operands that the launches between its
+copy's previous use have pushed out of L2 and the 256 MB Infinity Cache, so
+they come from HBM, while launches keep running back to back and the clock
+stays up. It gives the per-launch median, min and mean; for a workload whose
+figure of merit is its HBM rate (the skinny product and matrix-vector
+products) the roofline entry is taken from this mode. The GPU clock is sampled
+during both timed regions (``sclk_mhz``), and the run records the library file
+it loaded (path and hash) and the host CPU.
 
 Prints one JSON line. ``value`` is GFLOP/s (2*M*N*K per GEMM over the timed
 wall time). ``roofline`` reports the same kernel against the FP32-MFMA peak;
@@ -43,6 +50,84 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
 HOST_SECTION = "\n// Host side\n"
+# Workloads whose roofline entry is reported against the HBM peak from the
+# HBM-resident timing (besides every call below the ridge).
+HBM_FIGURE = {"skinny_16384x64x4096_nt"}
+# Bytes the HBM-resident mode rotates through (four times the Infinity Cache).
+ROTATE_BYTES = 5 << 28
+
+
+def file_sha16(path: str) -> str:
+    h = hashlib.sha256()
+    with open(path, "rb") as f:
+        for chunk in iter(lambda: f.read(1 << 20), b""):
+            h.update(chunk)
+    return h.hexdigest()[:16]
+
+
+def host_info() -> dict:
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        cores = os.cpu_count()
+    return {"cpu_model": model, "cores_available": cores}
+
+
+class ClockSampler:
+    """Samples the GPU's current graphics clock (MHz) every ~1 ms on a thread
+    while the context is open, through the AMD SMI library; reports the
+    samples' mean, min and max, or why it could not read them."""
+
+    def __init__(self):
+        self.samples, self.error, self._stop = [], None, None
+
+    def __enter__(self):
+        import threading
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init(amdsmi.AmdSmiInitFlags.INIT_AMD_GPUS)
+            handle = amdsmi.amdsmi_get_processor_handles()[0]
+            self._read = lambda: amdsmi.amdsmi_get_clock_info(
+                handle, amdsmi.AmdSmiClkType.SYS)["clk"]
+            self._read()
+        except Exception as e:  # noqa: BLE001 -- report, never fail the bench
+            self.error = f"{type(e).__name__}: {e}"
+            return self
+        self._stop = threading.Event()
+
+        def loop():
+            while not self._stop.is_set():
+                try:
+                    self.samples.append(float(self._read()))
+                except Exception as e:  # noqa: BLE001
+                    self.error = f"{type(e).__name__}: {e}"
+                    return
+                self._stop.wait(0.001)
+        self._thread = threading.Thread(target=loop, daemon=True)
+        self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        if self._stop is not None:
+            self._stop.set()
+            self._thread.join()
+        return False
+
+    def report(self):
+        if not self.samples:
+            return {"samples": 0, "error": self.error or "no samples"}
+        return {"samples": len(self.samples),
+                "mean": round(sum(self.samples) / len(self.samples), 1),
+                "min": min(self.samples), "max": max(self.samples)}
 
 
 def kernel_source_hash() -> str:
@@ -140,23 +225,78 @@ def copy_reference(torch, dev, args) -> int:
     return 0
 
 
-def roofline_entry(w, roof, achieved_tflops, peak_tflops, per_launch_ms, traffic):
+def roofline_entry(w, roof, achieved_tflops, peak_tflops, per_launch_ms, traffic,
+                   hbm_figure=False):
     """The roofline object of the report: against the FP32-MFMA peak for a call
-    above the ridge (every one of the five workloads), against the HBM peak in
-    GB/s of algorithmic bytes for one below it (a matrix-vector product)."""
+    above the ridge, against the HBM peak in GB/s of algorithmic bytes for one
+    below it (a matrix-vector product) or for a workload judged by its HBM rate
+    (`hbm_figure`: the skinny product, whose time is then that of the
+    HBM-resident launches; its MFMA fraction stays beside it)."""
     from precision_gemm_amd import measure
     gbs = w.algorithmic_bytes() / (per_launch_ms * 1e-3) / 1e9
     common = {"traffic": traffic, "arithmetic_intensity": round(roof.intensity, 2),
-              "kernel_ms": round(per_launch_ms, 5)}
-    if roof.bound == "memory-bound":
+              "kernel_ms": round(per_launch_ms, 5),
+              "timing": "hbm_resident" if hbm_figure else "back_to_back"}
+    if roof.bound == "memory-bound" or hbm_figure:
         peak_gbs = measure.MI355X_HBM_BW / 1e9
         return {"bound": "hbm", "achieved": round(gbs, 1), "peak": peak_gbs, "unit": "GB/s",
                 "frac": round(gbs / peak_gbs, 4), **common,
-                "tflops_at_achieved": round(achieved_tflops, 3)}
+                "tflops_at_achieved": round(achieved_tflops, 3),
+                "mfma_frac_at_achieved": round(achieved_tflops / peak_tflops, 4)}
     return {"bound": "mfma", "achieved": round(achieved_tflops, 3), "peak": peak_tflops,
             "unit": "TFLOP/s", "frac": round(achieved_tflops / peak_tflops, 4), **common,
             "hbm_gbs_at_achieved": round(gbs, 1),
             "hbm_frac_at_achieved": round(gbs * 1e9 / measure.MI355X_HBM_BW, 4)}
+
+
+def hbm_resident(torch, dev, stream, w, dA, dB, dC, launch, steps, min_warmup_ms):
+    """Time `steps` launches cycling through R copies of (A, B, C), R large
+    enough that the copies hold at least ROTATE_BYTES (at least 4 copies):
+    between two uses of one copy the other launches move more bytes than L2
+    and the Infinity Cache hold, so every launch reads its operands from HBM.
+    Each launch is bracketed by its own events, recorded back to back."""
+    per = 4 * (dA.numel() + dB.numel() + dC.numel())
+    copies = max(4, -(-ROTATE_BYTES // per))
+    As = dA.unsqueeze(0).repeat(copies, 1)
+    Bs = dB.unsqueeze(0).repeat(copies, 1)
+    Cs = dC.unsqueeze(0).repeat(copies, 1)
+
+    def one(i):
+        j = i % copies
+        launch(As[j], Bs[j], Cs[j])
+
+    i = 0
+    t0 = time.perf_counter()
+    while i < max(2 * copies, 8) or (time.perf_counter() - t0) * 1e3 < min_warmup_ms:
+        one(i)
+        i += 1
+        if i % 8 == 0:
+            torch.cuda.synchronize(dev)
+    torch.cuda.synchronize(dev)
+    events = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    with ClockSampler() as clock:
+        events[0].record(stream)
+        for k in range(steps):
+            one(i + k)
+            events[k + 1].record(stream)
+        torch.cuda.synchronize(dev)
+    ms = [events[k].elapsed_time(events[k + 1]) for k in range(steps)]
+    srt = sorted(ms)
+    med, mean = srt[len(srt) // 2], sum(ms) / len(ms)
+    gbs = lambda t: w.algorithmic_bytes() / (t * 1e-3) / 1e9  # noqa: E731
+    from precision_gemm_amd import measure
+    del As, Bs, Cs
+    return {
+        "copies": copies, "bytes_rotated": copies * per, "launches": steps,
+        "mean_ms": round(mean, 5), "median_ms": round(med, 5), "min_ms": round(srt[0], 5),
+        "tflops_at_median": round(w.flops() / (med * 1e-3) / 1e12, 3),
+        "tflops_at_mean": round(w.flops() / (mean * 1e-3) / 1e12, 3),
+        "alg_hbm_gbs_at_mean": round(gbs(mean), 1),
+        "alg_hbm_gbs_at_median": round(gbs(med), 1),
+        "hbm_frac_at_mean": round(gbs(mean) * 1e9 / measure.MI355X_HBM_BW, 4),
+        "hbm_frac_at_median": round(gbs(med) * 1e9 / measure.MI355X_HBM_BW, 4),
+        "sclk_mhz": clock.report(),
+    }
 
 
 def main(argv=None) -> int:
@@ -171,11 +311,16 @@ def main(argv=None) -> int:
                          "(the GPU clock takes tens of ms to ramp up under load)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate CPU time for the oracle baseline sample")
-    ap.add_argument("--cold-launches", type=int, default=20,
+    ap.add_argument("--cold-launches", type=int, default=0,
                     help="single launches timed after restoring C and flushing the caches "
                          "(reported as `cold`, not the headline; 0 skips them)")
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the oracle leg (profiling runs)")
+    ap.add_argument("--no-hbm-resident", action="store_true",
+                    help="skip the timing on rotated operand copies")
+    ap.add_argument("--hbm-only", action="store_true",
+                    help="launch only the rotated copies after the first launch (profiling "
+                         "the HBM-resident mode: no warm timed region, no determinism rerun)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="instead of SGEMM, time a plain device copy of this many MiB "
                          "(reference kernel for scaling HBM byte counters)")
@@ -203,15 +348,24 @@ def main(argv=None) -> int:
     dA, dB, dC = (torch.from_numpy(x).to(dev) for x in (A, B, C))
     stream = torch.cuda.current_stream(dev)
 
-    def step():
-        pg.sgemm_strided_batched_variant(w.trans_a, w.trans_b, w.M, w.N, w.K, w.alpha, dA,
-                                         w.LDA, dB, w.LDB, w.beta, dC, w.LDC, w.batch, w.SA,
+    def launch(a, b, c):
+        pg.sgemm_strided_batched_variant(w.trans_a, w.trans_b, w.M, w.N, w.K, w.alpha, a,
+                                         w.LDA, b, w.LDB, w.beta, c, w.LDC, w.batch, w.SA,
                                          w.SB, w.SC, args.variant, stream=stream.cuda_stream)
+
+    def step():
+        launch(dA, dB, dC)
 
     # First launch on pristine inputs: its output is what the oracle sample checks.
     step()
     torch.cuda.synchronize(dev)
     first_out = dC.cpu().numpy()
+    if args.hbm_only:
+        dC.copy_(torch.from_numpy(C).to(dev))
+        res = hbm_resident(torch, dev, stream, w, dA, dB, dC, launch, args.steps,
+                           args.min_warmup_ms)
+        print(json.dumps({"workload": w.name, "hbm_resident": res}), flush=True)
+        return 0
 
     # Untimed warm-up: the requested W steps, continued until the clock has
     # had min_warmup_ms to ramp up (the first launches run well below the
@@ -232,11 +386,12 @@ def main(argv=None) -> int:
     K = args.steps
     region0, region1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize(dev)
-    region0.record(stream)
-    for _ in range(K):
-        step()
-    region1.record(stream)
-    torch.cuda.synchronize(dev)
+    with ClockSampler() as clock:
+        region0.record(stream)
+        for _ in range(K):
+            step()
+        region1.record(stream)
+        torch.cuda.synchronize(dev)
 
     total_ms = region0.elapsed_time(region1)
 
@@ -246,6 +401,11 @@ def main(argv=None) -> int:
     step()
     torch.cuda.synchronize(dev)
     identical = bool((dC.cpu().numpy().view("u4") == first_out.view("u4")).all())
+
+    hbm = None
+    if not args.no_hbm_resident:
+        dC.copy_(torch.from_numpy(C).to(dev))
+        hbm = hbm_resident(torch, dev, stream, w, dA, dB, dC, launch, K, args.min_warmup_ms)
 
     # Cold launches (not the headline): before each one C is restored and a
     # 1 GiB fill evicts L2 and the Infinity Cache, so A, B and C come from HBM;
@@ -279,10 +439,15 @@ def main(argv=None) -> int:
     variant = args.variant if args.variant >= 0 else pg.sgemm_select_variant(
         w.trans_a, w.trans_b, w.M, w.N, w.K, w.batch, vec4_ok, props.multi_processor_count)
 
-    achieved = flops / (per_launch_ms * 1e-3) / 1e12
     peak = measure.MI355X_FP32_MFMA_PEAK / 1e12
     roof = measure.place_on_roofline(flops, w.algorithmic_bytes(), measure.MI355X_FP32_MFMA_PEAK,
-                            measure.MI355X_HBM_BW)
+                                     measure.MI355X_HBM_BW)
+    # The roofline entry's kernel time: the warm back-to-back launches, or
+    # for a workload judged by its HBM rate the HBM-resident launches (mean).
+    hbm_figure = hbm is not None and (w.name in HBM_FIGURE or roof.bound == "memory-bound")
+    roof_ms = hbm["mean_ms"] if hbm_figure else per_launch_ms
+    achieved = flops / (roof_ms * 1e-3) / 1e12
+    lib_path = pg.library_path()
     out = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -308,12 +473,17 @@ def main(argv=None) -> int:
             "cus": props.multi_processor_count,
         },
         "pct_of_fp32_mfma_peak": round(100.0 * value * 1e9 / measure.MI355X_FP32_MFMA_PEAK, 2),
-        "roofline": roofline_entry(w, roof, achieved, peak, per_launch_ms,
+        "roofline": roofline_entry(w, roof, achieved, peak, roof_ms,
                                    load_traffic(w.name, pg.VARIANT_NAMES.get(variant,
-                                                                              str(variant)))),
+                                                                              str(variant))),
+                                   hbm_figure),
+        "sclk_mhz": clock.report(),
+        "hbm_resident": hbm,
         "determinism": {"rerun_identical_bits": identical},
         "cold": cold,
         "software": {"torch": torch.__version__, "hip": getattr(torch.version, "hip", None)},
+        "library": {"path": os.path.relpath(lib_path, ROOT), "sha256_16": file_sha16(lib_path)},
+        "host": host_info(),
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

@@ -42,11 +42,14 @@
  *        batch -14, strideA -15, strideB -16, strideC -17 (negative).
  *        A leading dimension must be at least the stored row length
  *        (lda >= max(1, transA ? M : K), ldb >= max(1, transB ? K : N),
- *        ldc >= max(1, N)) and below 2^21 elements, which keeps every
- *        in-tile byte offset within 31 bits. A NULL pointer is an error only
- *        where it would be dereferenced. Nothing is launched on error.
- *        The variant-forcing entry points return -18 for an unknown variant
- *        or a 4-float variant the operands cannot use, whatever the
+ *        ldc >= max(1, N)); any larger int is accepted. (Most kernels keep
+ *        32-bit byte offsets inside a tile; a call with a leading dimension
+ *        of 2^21 or more runs a 64-bit-addressed tile instead, see
+ *        SGEMM_VARIANT_W64x64.) A NULL pointer is an error only where it
+ *        would be dereferenced. Nothing is launched on error.
+ *        The variant-forcing entry points return -18 for an unknown variant,
+ *        a 4-float variant the operands cannot use, or a variant with 32-bit
+ *        in-tile offsets for a leading dimension of 2^21 or more, whatever the
  *        position of their `variant` argument; the split-K entry points
  *        return -19 for an invalid split count, -20 for an invalid
  *        workspace and -21 for a workspace too small for a forced split,
@@ -125,7 +128,12 @@ enum sgemm_variant {
                                     vectors, 2 <= N <= 8, with transA == 0 (B either
                                     way), or a few rows, 2 <= M <= 8, with transB == 1
                                     (A either way); -18 for any other call */
-    SGEMM_VARIANT_COUNT = 11
+    SGEMM_VARIANT_W64x64 = 11,  /*  64 x  64 tile, 4 waves, 4-float loads, 64-bit addressing
+                                    with per-lane predicates instead of 32-bit buffer
+                                    offsets: any leading dimension (chosen for calls with
+                                    an ld of 2^21 or more) */
+    SGEMM_VARIANT_W64x64_V1 = 12,/* the same with 1-float loads (any alignment) */
+    SGEMM_VARIANT_COUNT = 13
 };
 
 /*
@@ -137,8 +145,10 @@ enum sgemm_variant {
  * after one normalization the entry points make first: a vector operand whose
  * k elements are adjacent is described contiguous in k (op(B) with N == 1,
  * transB == 0 and ldb == 1 as transB == 1, ldb == K; op(A) with M == 1,
- * transA == 1 and lda == 1 as transA == 0, lda == K; for 1 < K < 2^21), which
- * names the same memory.
+ * transA == 1 and lda == 1 as transA == 0, lda == K; for K > 1), which
+ * names the same memory. The leading dimensions are not among the arguments:
+ * a call with one of 2^21 or more runs SGEMM_VARIANT_W64x64 (or its 1-float
+ * form) in place of any tile or streaming variant returned here.
  */
 int sgemm_select_variant(int transA, int transB, int M, int N, int K, int batch,
                          int vec4_ok, int num_cus);
@@ -280,7 +290,7 @@ int sgemm_select_splits(int transA, int transB, int M, int N, int K, int batch,
  *   op(B)[k,j] = transB ? B[k*ldb + j] : B[j*ldb + k]
  *   C[i,j]     = C[j*ldc + i]
  * and lda >= max(1, transA ? K : M), ldb >= max(1, transB ? N : K),
- * ldc >= max(1, M), each below 2^21. Read by rows, a column-major matrix is
+ * ldc >= max(1, M). Read by rows, a column-major matrix is
  * its transpose, so the call runs the row-major kernels on
  * C^T = op(B)^T @ op(A)^T with the operands swapped: no data moves and the
  * results are those of the row-major call on the transposed problem.
@@ -300,6 +310,19 @@ int sgemm_colmajor_strided_batched(int transA, int transB, int M, int N, int K,
                                    int batch, long long strideA, long long strideB,
                                    long long strideC,
                                    sgemm_stream_t stream);
+
+/*
+ * Host-side check of the buffer-range bookkeeping the tile and streaming
+ * kernels use while their load window walks an operand (tests; no device
+ * call). A window starts `left_bytes` before the end of the operand and moves
+ * `step_bytes` per K-step; ranges[i] receives the range the kernels give the
+ * buffer resource of window i: the bytes from its start to the operand's end,
+ * at most 2^31 - 1 and at least 0. Returns 0, or -1 for step_bytes <= 0,
+ * nsteps < 0 or a NULL `ranges` with nsteps > 0. `ranges` is host memory of
+ * nsteps entries owned by the caller.
+ */
+int sgemm_window_ranges(long long left_bytes, int step_bytes, int nsteps,
+                        unsigned int *ranges);
 
 #ifdef __cplusplus
 }

@@ -19,10 +19,12 @@ __all__ = [
     "sgemm_batched", "sgemm_batched_variant", "sgemm_colmajor",
     "sgemm_colmajor_strided_batched", "pointer_array", "sgemm_ws", "sgemm_strided_batched_ws",
     "sgemm_strided_batched_ws_variant", "sgemm_workspace_size", "sgemm_select_splits",
-    "sgemm_status_string", "sgemm_select_variant", "matmul", "library_path",
+    "sgemm_status_string", "sgemm_select_variant", "sgemm_window_ranges", "matmul",
+    "library_path",
     "VARIANT_AUTO", "VARIANT_L256x128", "VARIANT_M128x128", "VARIANT_S64x64",
     "VARIANT_S64x64_V1", "VARIANT_T64x64", "VARIANT_L256x256", "VARIANT_S64x64_K2",
-    "VARIANT_M128x128_DMA", "VARIANT_T32x64", "VARIANT_T64x32", "VARIANT_GEMV", "VARIANT_COUNT", "VARIANT_NAMES",
+    "VARIANT_M128x128_DMA", "VARIANT_T32x64", "VARIANT_T64x32", "VARIANT_GEMV",
+    "VARIANT_W64x64", "VARIANT_W64x64_V1", "VARIANT_COUNT", "VARIANT_NAMES",
 ]
 
 VARIANT_AUTO = -1
@@ -37,10 +39,12 @@ VARIANT_M128x128_DMA = 7
 VARIANT_T32x64 = 8
 VARIANT_T64x32 = 9
 VARIANT_GEMV = 10
-VARIANT_COUNT = 11
+VARIANT_W64x64 = 11
+VARIANT_W64x64_V1 = 12
+VARIANT_COUNT = 13
 VARIANT_NAMES = {0: "L256x128", 1: "M128x128", 2: "S64x64", 3: "S64x64_V1", 4: "T64x64",
                  5: "L256x256", 6: "S64x64_K2", 7: "M128x128_DMA",
-                 8: "T32x64", 9: "T64x32", 10: "GEMV"}
+                 8: "T32x64", 9: "T64x32", 10: "GEMV", 11: "W64x64", 12: "W64x64_V1"}
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _lib = None
@@ -102,6 +106,8 @@ def _load():
     lib.sgemm_colmajor_strided_batched.restype = i
     lib.sgemm_colmajor_strided_batched.argtypes = [i, i, i, i, i, f, p, i, p, i, f, p, i, i,
                                                    ll, ll, ll, p]
+    lib.sgemm_window_ranges.restype = i
+    lib.sgemm_window_ranges.argtypes = [ll, i, i, ctypes.POINTER(ctypes.c_uint)]
     _lib = lib
     return lib
 
@@ -297,6 +303,16 @@ def sgemm_select_variant(transA, transB, M, N, K, batch, vec4_ok, num_cus) -> in
     """C ABI ``sgemm_select_variant`` (host-side dispatch decision)."""
     return _load().sgemm_select_variant(int(transA), int(transB), M, N, K, batch,
                                         int(bool(vec4_ok)), num_cus)
+
+
+def sgemm_window_ranges(left_bytes, step_bytes, nsteps):
+    """C ABI ``sgemm_window_ranges``: the buffer ranges the kernels give the
+    successive load windows of an operand (host-side, no device call). Returns
+    a list of nsteps ints; raises SgemmError on invalid arguments."""
+    out = (ctypes.c_uint * max(1, nsteps))()
+    st = _load().sgemm_window_ranges(int(left_bytes), int(step_bytes), int(nsteps), out)
+    _check(st, True)
+    return list(out[:nsteps])
 
 
 def matmul(A, B, C, alpha=1.0, beta=0.0, transA=False, transB=False, stream=None):

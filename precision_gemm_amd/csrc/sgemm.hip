@@ -66,7 +66,10 @@ constexpr uint32_t kOOB = 0x80000000u;     // any byte offset >= this is out of 
 constexpr uint32_t kMaxRange = 0x7fffffffu; // largest buffer range used
 constexpr int kRsrcWord3 = 0x00020000;     // gfx9 raw buffer, 32-bit data format
 constexpr int kNumXcd = 8;                 // MI355X: 8 XCDs x 32 CUs
-constexpr int kMaxLd = (1 << 21) - 1;      // keeps (255*ld + 256)*4 < 2^31
+// Largest leading dimension for which every in-tile byte offset of the
+// buffer-resource kernels, (255*ld + 256)*4 at most, stays below 2^31. Calls
+// with a larger one run the 64-bit-addressed tile (the W64x64 variants).
+constexpr int kMaxLd = (1 << 21) - 1;
 
 // Batch item b's operands are A + b*sA, B + b*sB, C + b*sC, or, where the
 // pointer-array form supplies them, Aarr[b], Barr[b], Carr[b].
@@ -87,6 +90,9 @@ struct Params {
     // item b / splits and K slice b % splits, covering k in [s*kslice,
     // min((s+1)*kslice, K)); its partial tile goes to C item b.
     int splits, kslice;
+    // GEMV kernels only: the first output row of this launch (a launch covers
+    // at most 2^31 - 1 work-items, so a very tall matrix takes several).
+    int row_base;
 };
 
 __device__ __forceinline__ const float *item_a(const Params &p, int b)
@@ -124,6 +130,57 @@ __device__ void plain_tile(const Params &p, const float *Ab, const float *Bb, fl
     }
 }
 
+// Buffer range of an operand window that moves `step` bytes per K-step: the
+// bytes from the window's start to the end of the operand, capped at
+// 2^31 - 1 (the largest range used). While `big` is positive the window is
+// still capped; after that `rem` holds the exact bytes left, and stays at 0
+// once the window is past the end. Both advance with 32-bit scalar arithmetic
+// only. A K loop takes far fewer than 2^31 steps, so `big` saturates at
+// INT32_MAX.
+struct WindowRange {
+    int32_t big, rem, step;
+
+    __host__ __device__ __forceinline__ void init(long long left, int32_t step_bytes)
+    {
+        step = step_bytes;
+        if (left > (long long)kMaxRange) {
+            const long long capped = (left - kMaxRange + step_bytes - 1) / step_bytes;
+            if (capped >= (long long)INT32_MAX) {
+                big = INT32_MAX;
+                rem = (int32_t)kMaxRange;
+            } else {
+                const long long r = left - capped * step_bytes;
+                big = (int32_t)capped;
+                rem = r < 0 ? 0 : (int32_t)r;
+            }
+        } else {
+            big = 0;
+            rem = left < 0 ? 0 : (int32_t)left;
+        }
+    }
+    // Range of the current window, then move to the next one (rem >= 0
+    // throughout, so rem - step cannot overflow).
+    __host__ __device__ __forceinline__ uint32_t take()
+    {
+        const bool capped = big > 0;
+        const uint32_t range = capped ? kMaxRange : (uint32_t)rem;
+        big -= 1;
+        rem = capped ? rem : (rem > step ? rem - step : 0);
+        return range;
+    }
+};
+
+// Loads through the global address space (the item pointers arrive as
+// generic pointers, which would otherwise become flat loads).
+__device__ __forceinline__ f32x4 global_load4(const float *q)
+{
+    return *(const __attribute__((address_space(1))) f32x4 *)q;
+}
+__device__ __forceinline__ float global_load1(const float *q)
+{
+    return *(const __attribute__((address_space(1))) float *)q;
+}
+
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const float *base, long long elems)
 {
     long long bytes = elems * 4;
@@ -151,8 +208,12 @@ __device__ __forceinline__ void store1(__amdgpu_buffer_rsrc_t r, uint32_t off, f
 // One operand's K-step tile: global -> registers -> LDS, and LDS -> MFMA
 // operands. KC: k is the contiguous dimension of the stored operand.
 // BO: outer extent of the tile (BM for A, BN for B). VEC: floats per load.
+// WIDE: 64-bit element offsets and plain global loads under a per-lane
+// predicate instead of 32-bit buffer offsets, for leading dimensions too
+// large for the latter (any ld then works; the loop does 64-bit address
+// arithmetic, so only calls that need it take this form).
 // ---------------------------------------------------------------------------
-template <bool KC, int BO, int BK, int NT, int VEC>
+template <bool KC, int BO, int BK, int NT, int VEC, bool WIDE = false>
 struct Operand {
     static constexpr int PAD = 0;                        // outer-contiguous row padding
     static constexpr int ROW = KC ? BK : BO + PAD;       // LDS row length (floats)
@@ -175,19 +236,15 @@ struct Operand {
     long long total;  // elements from X to one past the last stored element
     int O, K;         // outer extent and K of the product
     int o0;           // first outer index of this tile
-    uint32_t off[NOFF];
+    // Per-lane offsets from the window start: bytes, kOOB for a lane outside
+    // the tile's outer range; WIDE: elements, -1 for such a lane.
+    std::conditional_t<WIDE, long long, uint32_t> off[NOFF];
     // Window of the next K-step to load: its first element and first k. The
     // first window starts at k = kfirst <= 0, so that a K that is not a
     // multiple of BK leaves its partial step first and every later step full.
-    // The buffer range of a window is the bytes left from its start to the
-    // end of the operand, capped at 2^31 - 1: while `big` is positive the
-    // window is capped, after that `rem` holds the exact bytes left (negative
-    // once past the end). Both advance with 32-bit scalar arithmetic only.
     const float *wp;
     int kn;
-    int32_t big;
-    int32_t rem;
-    int32_t step_bytes;
+    WindowRange win;
 
     __device__ __forceinline__ static int swz(int r) { return (r / SWZ_ROWS) % (BK / 4); }
 
@@ -208,7 +265,10 @@ struct Operand {
                 // KC: row r is outer index o0+r and the chunk runs along k;
                 // otherwise row r is a k index and the chunk runs along outer.
                 const bool ok = KC ? (o0 + r < O) : (o0 + 4 * c4 + e < O);
-                off[s * EPS + e] = ok ? (uint32_t)((elem + e) * 4) : kOOB;
+                if constexpr (WIDE)
+                    off[s * EPS + e] = ok ? elem + e : -1;
+                else
+                    off[s * EPS + e] = ok ? (uint32_t)((elem + e) * 4) : kOOB;
             }
         }
         // (kfirst < 0 moves the first window before the tile's k = 0; the
@@ -217,16 +277,8 @@ struct Operand {
                                (KC ? (long long)kfirst : (long long)kfirst * ld);
         wp = reinterpret_cast<const float *>(reinterpret_cast<uintptr_t>(X) + 4 * base);
         kn = kfirst;
-        step_bytes = (int32_t)(KC ? 4LL * BK : 4LL * BK * ld);
-        const long long left = 4 * (total - base);
-        if (left > (long long)kMaxRange) {
-            const long long capped = (left - kMaxRange + step_bytes - 1) / step_bytes;
-            big = (int32_t)capped;
-            rem = (int32_t)(left - capped * step_bytes);
-        } else {
-            big = 0;
-            rem = (int32_t)left;
-        }
+        if constexpr (!WIDE)
+            win.init(4 * (total - base), (int32_t)(KC ? 4LL * BK : 4LL * BK * ld));
     }
 
     // Issue the loads of the next K-step into regs and advance the window.
@@ -234,8 +286,36 @@ struct Operand {
     template <bool TAIL>
     __device__ __forceinline__ void load_next(int tid, f32x4 (&regs)[SLOTS])
     {
-        const bool capped = big > 0;
-        const uint32_t range = capped ? kMaxRange : (rem > 0 ? (uint32_t)rem : 0u);
+        if constexpr (WIDE) {
+            // Every step after the first is full and the first ends inside
+            // [0, K), so a step starting at k >= K is wholly past the end
+            // (the loads issued ahead of the last steps).
+            const bool step_ok = kn < K;
+#pragma unroll
+            for (int s = 0; s < SLOTS; ++s) {
+                const int f = tid + s * NT, r = f / C4, c4 = f % C4;
+                f32x4 v = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                for (int e = 0; e < EPS; ++e) {
+                    const long long o = off[s * EPS + e];
+                    bool ok = step_ok && o >= 0;
+                    if (TAIL)
+                        ok = ok && (uint32_t)(KC ? kn + 4 * c4 + (VEC == 4 ? 0 : e) : kn + r) <
+                                       (uint32_t)K;
+                    if (VEC == 4) {
+                        if (ok)
+                            v = global_load4(wp + o);
+                    } else if (ok) {
+                        v[e] = global_load1(wp + o);
+                    }
+                }
+                regs[s] = v;
+            }
+            wp += KC ? (long long)BK : (long long)BK * ld;
+            kn += BK;
+            return;
+        }
+        const uint32_t range = win.take();
         const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
             const_cast<float *>(wp), (short)0, (int)range, kRsrcWord3);
 #pragma unroll
@@ -260,8 +340,6 @@ struct Operand {
         }
         wp += KC ? (long long)BK : (long long)BK * ld;
         kn += BK;
-        big -= 1;
-        rem -= capped ? 0 : step_bytes;
     }
 
     __device__ __forceinline__ static void store(float *lds, int tid, const f32x4 (&regs)[SLOTS])
@@ -318,11 +396,31 @@ __device__ __forceinline__ void tile_of(const Params &p, int &b, int &tm, int &t
 // res[i][j][vv] is accumulator register v0 + vv of the wave's MFMA tile (i, j):
 // register v of lane l holds row 8*(v/4) + 4*(l/32) + v%4, column l%32 of the
 // 32 x 32 product at (wm0 + 32 i, wn0 + 32 j) inside the workgroup tile.
-template <int TM, int TN, int VN>
+template <int TM, int TN, int VN, bool WIDE = false>
 __device__ __forceinline__ void store_tile(const Params &p, float *Cb, int m0, int n0, int wm0,
                                            int wn0, int v0, int lane,
                                            const float (&res)[TM][TN][VN])
 {
+    if constexpr (WIDE) {
+        // 64-bit addresses; lanes outside M x N store nothing.
+        const int g = lane >> 5;
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+#pragma unroll
+                for (int vv = 0; vv < VN; ++vv) {
+                    const int v = v0 + vv;
+                    const int row = m0 + wm0 + 32 * i + 8 * (v >> 2) + 4 * g + (v & 3);
+                    const int col = n0 + wn0 + 32 * j + (lane & 31);
+                    if (row < p.M && col < p.N) {
+                        float *c = Cb + (long long)row * p.ldc + col;
+                        *c = p.beta == 0.0f ? p.alpha * res[i][j][vv]
+                                            : __builtin_fmaf(p.alpha, res[i][j][vv], p.beta * *c);
+                    }
+                }
+        return;
+    }
     const long long cbase = (long long)m0 * p.ldc + n0;
     const __amdgpu_buffer_rsrc_t rc =
         make_rsrc(Cb + cbase, (long long)(p.M - 1) * p.ldc + p.N - cbase);
@@ -346,11 +444,13 @@ __device__ __forceinline__ void store_tile(const Params &p, float *Cb, int m0, i
                     if (with_beta)
                         c[vv] = load1(rc, off[vv]);
                 }
+                // alpha * acc, or fma(alpha, acc, beta * c): one rounding
+                // order for every tile kernel, whatever the compiler contracts.
 #pragma unroll
                 for (int vv = 0; vv < VN; ++vv) {
-                    float out = p.alpha * res[i][j][vv];
-                    if (with_beta)
-                        out += p.beta * c[vv];
+                    const float out = with_beta
+                                          ? __builtin_fmaf(p.alpha, res[i][j][vv], p.beta * c[vv])
+                                          : p.alpha * res[i][j][vv];
                     store1(rc, off[vv], out);
                 }
             }
@@ -369,7 +469,7 @@ __device__ __forceinline__ void store_tile(const Params &p, float *Cb, int m0, i
 // the end in a fixed order (group 0's plus group 1's), so results do not
 // depend on timing.
 template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int WAVES_K, int MIN_WAVES_PER_EU,
-          bool A_KC, bool B_KC, int VEC>
+          bool A_KC, bool B_KC, int VEC, bool WIDE>
 __global__ void
 __attribute__((amdgpu_flat_work_group_size(64 * WAVES_M * WAVES_N * WAVES_K,
                                            64 * WAVES_M * WAVES_N * WAVES_K),
@@ -382,8 +482,8 @@ sgemm_mfma_kernel(Params p)
     constexpr int TM = WM / 32, TN = WN / 32;
     static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tile must be a multiple of 32");
     static_assert(WAVES_K == 1 || WAVES_K == 2, "WAVES_K");
-    using OpA = Operand<A_KC, BM, BK, NT, VEC>;
-    using OpB = Operand<B_KC, BN, BK, NT, VEC>;
+    using OpA = Operand<A_KC, BM, BK, NT, VEC, WIDE>;
+    using OpB = Operand<B_KC, BN, BK, NT, VEC, WIDE>;
 
     // Two stages, each holding the A tile followed by the B tile.
     constexpr int STAGE = OpA::STAGE + OpB::STAGE;
@@ -594,7 +694,7 @@ sgemm_mfma_kernel(Params p)
                 }
     }
 
-    store_tile<TM, TN, VN>(p, Cb, m0, n0, wm0, wn0, v0, lane, res);
+    store_tile<TM, TN, VN, WIDE>(p, Cb, m0, n0, wm0, wn0, v0, lane, res);
 }
 
 // ---------------------------------------------------------------------------
@@ -633,11 +733,10 @@ struct DmaOperand {
     int wv;               // this wave's index among the NW sharing the tile
     uint32_t off[NBW];    // this lane's chunk in each of its blocks, relative to the step's window
     // Window of this wave's next K-step (the waves of a workgroup take every
-    // WAVES-th step): first element and first k, and its buffer range kept as
-    // in Operand (`big` windows capped at 2^31 - 1, then `rem` exact bytes).
+    // WAVES-th step): first element and first k, and its buffer range.
     const float *wp;
     int kn, kstep;
-    int32_t big, rem, step_bytes;
+    WindowRange win;
     long long step_elems;
 
     __device__ __forceinline__ static int swz(int r) { return (r / SWZ_ROWS) % (BK / 4); }
@@ -670,16 +769,7 @@ struct DmaOperand {
         kn = k0;
         kstep = kstride;
         step_elems = KC ? (long long)kstride : (long long)kstride * ld;
-        step_bytes = (int32_t)(4 * step_elems);
-        const long long left = 4 * (total - base);
-        if (left > (long long)kMaxRange) {
-            const long long capped = (left - kMaxRange + step_bytes - 1) / step_bytes;
-            big = (int32_t)capped;
-            rem = (int32_t)(left - capped * step_bytes);
-        } else {
-            big = 0;
-            rem = left < 0 ? 0 : (int32_t)left;
-        }
+        win.init(4 * (total - base), (int32_t)(4 * step_elems));
     }
 
     // Load this wave's next K-step into `tile` and advance the window.
@@ -688,8 +778,7 @@ struct DmaOperand {
     template <bool TAIL>
     __device__ __forceinline__ void issue(float *tile, int lane)
     {
-        const bool capped = big > 0;
-        const uint32_t range = capped ? kMaxRange : (rem > 0 ? (uint32_t)rem : 0u);
+        const uint32_t range = win.take();
         const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
             const_cast<float *>(wp), (short)0, (int)range, kRsrcWord3);
 #pragma unroll
@@ -707,8 +796,6 @@ struct DmaOperand {
         }
         wp += step_elems;
         kn += kstep;
-        big -= 1;
-        rem -= capped ? 0 : step_bytes;
     }
 
     // Same operand layout contract as Operand::frag (k permuted within groups of 8).
@@ -1140,19 +1227,12 @@ sgemm_dma_kernel(Params p)
 // chunks of k round-robin, keeping UNROLL chunks of every row in flight, and
 // the partial sums are added across each wave with lane exchanges and across
 // the four waves in LDS, always in the same order.
-// 16-byte load through the global address space (the item pointers arrive
-// as generic pointers, which would otherwise become flat loads).
-__device__ __forceinline__ f32x4 global_load4(const float *q)
-{
-    return *(const __attribute__((address_space(1))) f32x4 *)q;
-}
-
 template <int ROWS>
 __global__ void __launch_bounds__(256) sgemv_kernel(Params p)
 {
     constexpr int T = 256, UNROLL = 4, WAVES = T / 64;
     const int b = blockIdx.y;
-    const int m0 = blockIdx.x * ROWS;
+    const int m0 = p.row_base + blockIdx.x * ROWS;
     const int t = threadIdx.x;
     const float *A = item_a(p, b), *x = item_b(p, b);
     float *C = item_c(p, b);
@@ -1237,7 +1317,7 @@ __global__ void __launch_bounds__(256) sgemv_nv_kernel(Params p)
 {
     constexpr int T = 256, WAVES = T / 64;
     const int b = blockIdx.y;
-    const int m0 = blockIdx.x * ROWS;
+    const int m0 = p.row_base + blockIdx.x * ROWS;
     const int t = threadIdx.x;
     const int N = p.N;
     const float *A = item_a(p, b), *B = item_b(p, b);
@@ -1332,11 +1412,6 @@ __global__ void __launch_bounds__(256) sgemv_nv_kernel(Params p)
     }
 }
 
-__device__ __forceinline__ float global_load1(const float *q)
-{
-    return *(const __attribute__((address_space(1))) float *)q;
-}
-
 // Matrix-vector product with the matrix contiguous along the outputs, the
 // N == 1 case with A stored K x M: y[m] = alpha * sum_k A[k * lda + m] x[k] +
 // beta * y[m], x the K floats of op(B), y[m] at C[m * ldc]. A workgroup owns
@@ -1355,7 +1430,7 @@ __global__ void __launch_bounds__(512) sgemv_t_kernel(Params p)
     const int xcd = pid % kNumXcd, local = pid / kNumXcd;
     const int q = num / kNumXcd, r = num % kNumXcd;
     const int blk = xcd < r ? xcd * (q + 1) + local : r * (q + 1) + (xcd - r) * q + local;
-    const int m0 = blk * BC;
+    const int m0 = p.row_base + blk * BC;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int cg = lane % LPR, ro = lane / LPR;
     const int m = m0 + 4 * cg; // the host guarantees M % 4 == 0 and lda % 4 == 0
@@ -1475,14 +1550,14 @@ struct VariantInfo {
 
 constexpr int kBK = 16;
 
-template <int BM, int BN, int BK, int WM_, int WN_, int WK_, int MW, int VEC>
+template <int BM, int BN, int BK, int WM_, int WN_, int WK_, int MW, int VEC, bool WIDE = false>
 constexpr VariantInfo make_variant()
 {
     return VariantInfo{BM, BN, BK, 64 * WM_ * WN_ * WK_, VEC,
-                       {{sgemm_mfma_kernel<BM, BN, BK, WM_, WN_, WK_, MW, true, false, VEC>,
-                         sgemm_mfma_kernel<BM, BN, BK, WM_, WN_, WK_, MW, true, true, VEC>},
-                        {sgemm_mfma_kernel<BM, BN, BK, WM_, WN_, WK_, MW, false, false, VEC>,
-                         sgemm_mfma_kernel<BM, BN, BK, WM_, WN_, WK_, MW, false, true, VEC>}}};
+                       {{sgemm_mfma_kernel<BM, BN, BK, WM_, WN_, WK_, MW, true, false, VEC, WIDE>,
+                         sgemm_mfma_kernel<BM, BN, BK, WM_, WN_, WK_, MW, true, true, VEC, WIDE>},
+                        {sgemm_mfma_kernel<BM, BN, BK, WM_, WN_, WK_, MW, false, false, VEC, WIDE>,
+                         sgemm_mfma_kernel<BM, BN, BK, WM_, WN_, WK_, MW, false, true, VEC, WIDE>}}};
 }
 
 template <int BM, int BN, int WM_, int WN_, int MW>
@@ -1519,7 +1594,15 @@ const VariantInfo kVariants[SGEMM_VARIANT_COUNT] = {
     // SGEMM_VARIANT_GEMV: N == 1 (or M == 1, as its transpose) with the vector
     // contiguous in k; launched by launch_gemv, which picks the kernel.
     VariantInfo{4, 1, 4, 256, 4, {{nullptr, sgemv_kernel<4>}, {nullptr, sgemv_t_kernel<64>}}},
+    make_variant<64, 64, kBK, 2, 2, 1, 4, 4, true>(), // SGEMM_VARIANT_W64x64
+    make_variant<64, 64, kBK, 2, 2, 1, 4, 1, true>(), // SGEMM_VARIANT_W64x64_V1
 };
+
+// The 64-bit-addressed builds, which take any leading dimension.
+bool is_wide(int variant)
+{
+    return variant == SGEMM_VARIANT_W64x64 || variant == SGEMM_VARIANT_W64x64_V1;
+}
 
 long long ceil_div(long long a, long long b) { return (a + b - 1) / b; }
 
@@ -1568,9 +1651,9 @@ int validate(int tA, int tB, int M, int N, int K, const float *A, int lda, const
     if (N < 0) return -4;
     if (K < 0) return -5;
     const int rowA = tA ? M : K, rowB = tB ? K : N;
-    if (lda < (rowA > 1 ? rowA : 1) || lda > kMaxLd) return -8;
-    if (ldb < (rowB > 1 ? rowB : 1) || ldb > kMaxLd) return -10;
-    if (ldc < (N > 1 ? N : 1) || ldc > kMaxLd) return -13;
+    if (lda < (rowA > 1 ? rowA : 1)) return -8;
+    if (ldb < (rowB > 1 ? rowB : 1)) return -10;
+    if (ldc < (N > 1 ? N : 1)) return -13;
     if (batch < 0) return -14;
     if (sA < 0) return -15;
     if (sB < 0) return -16;
@@ -1799,11 +1882,11 @@ int launch(const Call &c, int variant, hipStream_t s, Split sk = Split{nullptr, 
     // (likewise op(A) with M == 1, transA == 1, lda == 1). That description
     // allows the 16-byte loads along k.
     Call cc = c;
-    if (cc.N == 1 && cc.tB == 0 && cc.ldb == 1 && cc.K > 1 && cc.K <= kMaxLd) {
+    if (cc.N == 1 && cc.tB == 0 && cc.ldb == 1 && cc.K > 1) {
         cc.tB = 1;
         cc.ldb = cc.K;
     }
-    if (cc.M == 1 && cc.tA == 1 && cc.lda == 1 && cc.K > 1 && cc.K <= kMaxLd) {
+    if (cc.M == 1 && cc.tA == 1 && cc.lda == 1 && cc.K > 1) {
         cc.tA = 0;
         cc.lda = cc.K;
     }
@@ -1821,7 +1904,7 @@ int launch_gemv(const Call &c, hipStream_t s, bool c_transposed)
     if (st != 0)
         return st;
     long long blocks;
-    int threads;
+    int threads, rows_per_block;
     KernelFn fn;
     if (c.N > 1) {
         // A few vectors (2 <= N <= 8, A contiguous in k): four rows per
@@ -1845,12 +1928,14 @@ int launch_gemv(const Call &c, hipStream_t s, bool c_transposed)
         // (B stored K x N: the host guarantees N % 4 == 0, so nv == N.)
         fn = c.tB == 1 ? kc[c_transposed][four][nv == 2 ? 0 : nv == 4 ? 1 : 2]
                        : kn[c_transposed][four][nv == 4 ? 0 : 1];
-        blocks = ceil_div(c.M, four ? 4 : 1);
+        rows_per_block = four ? 4 : 1;
+        blocks = ceil_div(c.M, rows_per_block);
         threads = 256;
     } else if (c.tA == 0) {
         // Four rows per workgroup, or one when that leaves fewer than two
         // workgroups per CU.
         const int rows = ceil_div(c.M, 4) * c.batch >= 2LL * cus ? 4 : 1;
+        rows_per_block = rows;
         blocks = ceil_div(c.M, rows);
         threads = 256;
         fn = rows == 4 ? sgemv_kernel<4> : sgemv_kernel<1>;
@@ -1868,14 +1953,13 @@ int launch_gemv(const Call &c, hipStream_t s, bool c_transposed)
                        : ceil_div(c.M, 16) * c.batch >= cus                  ? 16
                        : ceil_div(c.M, 8) * c.batch >= cus || c.K < 16384 ? 8
                                                                              : 4;
+        rows_per_block = bc;
         blocks = ceil_div(c.M, bc);
         threads = 512;
         static const KernelFn kt[5] = {sgemv_t_kernel<4>, sgemv_t_kernel<8>, sgemv_t_kernel<16>,
                                        sgemv_t_kernel<32>, sgemv_t_kernel<64>};
         fn = kt[bc == 4 ? 0 : bc == 8 ? 1 : bc == 16 ? 2 : bc == 32 ? 3 : 4];
     }
-    if (blocks * threads > INT32_MAX)
-        return -22;
     Params p{};
     p.A = c.A;
     p.B = c.B;
@@ -1900,23 +1984,31 @@ int launch_gemv(const Call &c, hipStream_t s, bool c_transposed)
     p.splits = 1;
     p.kslice = c.K;
     const bool arrays = c.Aarr != nullptr;
+    // A launch holds at most 2^31 - 1 work-items along grid x: a taller
+    // matrix runs as several launches over consecutive row blocks, each told
+    // its first row (the kernels keep M itself for the bounds).
+    const long long max_blocks = INT32_MAX / threads;
     for (long long b0 = 0; b0 < c.batch; b0 += 65535) {
         const long long nb = c.batch - b0 < 65535 ? c.batch - b0 : 65535;
-        Params q = p;
-        if (arrays) {
-            q.Aarr = c.Aarr + b0;
-            q.Barr = c.Barr + b0;
-            q.Carr = c.Carr + b0;
-        } else {
-            q.A = c.A + b0 * c.sA;
-            q.B = c.B + b0 * c.sB;
-            q.C = c.C + b0 * c.sC;
+        for (long long k0 = 0; k0 < blocks; k0 += max_blocks) {
+            const long long nk = blocks - k0 < max_blocks ? blocks - k0 : max_blocks;
+            Params q = p;
+            q.row_base = (int)(k0 * rows_per_block);
+            if (arrays) {
+                q.Aarr = c.Aarr + b0;
+                q.Barr = c.Barr + b0;
+                q.Carr = c.Carr + b0;
+            } else {
+                q.A = c.A + b0 * c.sA;
+                q.B = c.B + b0 * c.sB;
+                q.C = c.C + b0 * c.sC;
+            }
+            void *args[] = {&q};
+            hipError_t e = hipLaunchKernel((const void *)fn, dim3((unsigned)nk, (unsigned)nb),
+                                           dim3(threads), args, 0, s);
+            if (e != hipSuccess)
+                return (int)e;
         }
-        void *args[] = {&q};
-        hipError_t e = hipLaunchKernel((const void *)fn, dim3((unsigned)blocks, (unsigned)nb),
-                                       dim3(threads), args, 0, s);
-        if (e != hipSuccess)
-            return (int)e;
     }
     return 0;
 }
@@ -1939,11 +2031,18 @@ int launch_canonical(const Call &c, int variant, hipStream_t s, Split sk)
         if (st != 0)
             return st;
     }
+    // A leading dimension beyond kMaxLd overflows the 32-bit in-tile offsets
+    // of every kernel but the 64-bit-addressed tile and the GEMV kernels
+    // (which address with 64-bit arithmetic throughout).
+    const bool wide = c.lda > kMaxLd || c.ldb > kMaxLd || c.ldc > kMaxLd;
     if (auto_variant) {
         variant = sgemm_select_variant(c.tA, c.tB, c.M, c.N, c.K, c.batch, vec4_ok ? 1 : 0, cus);
         if (variant < 0)
             return variant;
-    } else if (kVariants[variant].vec == 4 && !vec4_ok) {
+        if (wide && variant != SGEMM_VARIANT_GEMV)
+            variant = vec4_ok ? SGEMM_VARIANT_W64x64 : SGEMM_VARIANT_W64x64_V1;
+    } else if ((kVariants[variant].vec == 4 && !vec4_ok) ||
+               (wide && !is_wide(variant) && variant != SGEMM_VARIANT_GEMV)) {
         return -18;
     }
     if (variant == SGEMM_VARIANT_GEMV) {
@@ -2030,7 +2129,7 @@ int launch_canonical(const Call &c, int variant, hipStream_t s, Split sk)
     const long long tiles_item = ceil_div(c.M, vi.bm) * ceil_div(c.N, vi.bn);
     if (tiles_item * vi.threads > INT32_MAX || (long long)splits * tiles_item > INT32_MAX)
         return -22;
-    Params p;
+    Params p{};
     p.A = c.A;
     p.B = c.B;
     p.C = c.C;
@@ -2121,9 +2220,9 @@ int validate_colmajor(int tA, int tB, int M, int N, int K, const float *A, int l
     if (N < 0) return -4;
     if (K < 0) return -5;
     const int colA = tA ? K : M, colB = tB ? N : K;
-    if (lda < (colA > 1 ? colA : 1) || lda > kMaxLd) return -8;
-    if (ldb < (colB > 1 ? colB : 1) || ldb > kMaxLd) return -10;
-    if (ldc < (M > 1 ? M : 1) || ldc > kMaxLd) return -13;
+    if (lda < (colA > 1 ? colA : 1)) return -8;
+    if (ldb < (colB > 1 ? colB : 1)) return -10;
+    if (ldc < (M > 1 ? M : 1)) return -13;
     if (batch < 0) return -14;
     if (sA < 0) return -15;
     if (sB < 0) return -16;
@@ -2305,6 +2404,18 @@ extern "C" int sgemm_colmajor(int transA, int transB, int M, int N, int K, float
                                           ldc, 1, 0, 0, 0, stream);
 }
 
+extern "C" int sgemm_window_ranges(long long left_bytes, int step_bytes, int nsteps,
+                                   unsigned int *ranges)
+{
+    if (step_bytes <= 0 || nsteps < 0 || (nsteps > 0 && ranges == nullptr))
+        return -1;
+    WindowRange w;
+    w.init(left_bytes, step_bytes);
+    for (int i = 0; i < nsteps; ++i)
+        ranges[i] = w.take();
+    return 0;
+}
+
 extern "C" const char *sgemm_status_string(int status)
 {
     switch (status) {
@@ -2315,16 +2426,16 @@ extern "C" const char *sgemm_status_string(int status)
     case -4: return "invalid argument 4 (N < 0)";
     case -5: return "invalid argument 5 (K < 0)";
     case -7: return "invalid argument 7 (A or A_array is NULL)";
-    case -8: return "invalid argument 8 (lda below the stored row length or >= 2^21)";
+    case -8: return "invalid argument 8 (lda below the stored row length)";
     case -9: return "invalid argument 9 (B or B_array is NULL)";
-    case -10: return "invalid argument 10 (ldb below the stored row length or >= 2^21)";
+    case -10: return "invalid argument 10 (ldb below the stored row length)";
     case -12: return "invalid argument 12 (C or C_array is NULL)";
-    case -13: return "invalid argument 13 (ldc below the stored row length or >= 2^21)";
+    case -13: return "invalid argument 13 (ldc below the stored row length)";
     case -14: return "invalid argument 14 (batch < 0)";
     case -15: return "invalid argument 15 (strideA < 0)";
     case -16: return "invalid argument 16 (strideB < 0)";
     case -17: return "invalid argument 17 (strideC < 0)";
-    case -18: return "invalid variant argument (unknown variant, or a 4-float variant for unaligned operands)";
+    case -18: return "invalid variant argument (unknown variant, a 4-float variant for unaligned operands, or a 32-bit-offset variant for a leading dimension of 2^21 or more)";
     case -19: return "invalid split count (negative, over 65535, or a split of the streaming variant)";
     case -20: return "invalid workspace (NULL or not 4-byte aligned while workspace_bytes > 0)";
     case -21: return "workspace too small for the requested split count";

@@ -135,16 +135,17 @@ def sweep(shapes, rounds: int = 3, target_ms: float = 20.0, out=sys.stdout):
         # against a matrix contiguous in k, or the mirror), follow that
         # description.
         cA, cB = tA, tB
-        if N == 1 and tB == 0 and ldb == 1 and 1 < K < 1 << 21:
+        if N == 1 and tB == 0 and ldb == 1 and 1 < K:
             cB = 1
-        if M == 1 and tA == 1 and lda == 1 and 1 < K < 1 << 21:
+        if M == 1 and tA == 1 and lda == 1 and 1 < K:
             cA = 0
         gemv_ok = ((N == 1 and cB == 1) or (M == 1 and cA == 0) or
                    (2 <= N <= 8 and cA == 0 and (cB == 1 or N % 4 == 0)) or
                    (2 <= M <= 8 and cB == 1 and (cA == 0 or M % 4 == 0)))
         auto = pg.sgemm_select_variant(cA, cB, M, N, K, batch, 1, cus)
-        variants = [v for v in range(pg.VARIANT_COUNT) if v != pg.VARIANT_S64x64_V1 and
-                    (v != pg.VARIANT_GEMV or gemv_ok)]
+        variants = [v for v in range(pg.VARIANT_COUNT)
+                    if v not in (pg.VARIANT_S64x64_V1, pg.VARIANT_W64x64, pg.VARIANT_W64x64_V1)
+                    and (v != pg.VARIANT_GEMV or gemv_ok)]
 
         def caller(v):
             return lambda: pg.sgemm_strided_batched_variant(

@@ -63,6 +63,38 @@ def test_header_compiles_as_c():
                    input=src, text=True, check=True)
 
 
+WINDOW_CAP = (1 << 31) - 1
+
+
+def expected_ranges(left, step, n):
+    """Window i starts i * step bytes further in: the bytes left from there to
+    the operand's end, within [0, 2^31 - 1]."""
+    return [min(max(left - i * step, 0), WINDOW_CAP) for i in range(n)]
+
+
+@pytest.mark.parametrize("step", [64, 4096, 64 * 4092, 64 * ((1 << 21) - 1), 512 * 4096])
+def test_window_ranges_match_the_bytes_left(pg, step):
+    """The buffer-range countdown the kernels keep per operand window, for
+    operands from a few bytes to 300 GiB past the window start, including every
+    crossing of the 2^31 cap, against the exact bytes left."""
+    GiB = 1 << 30
+    lefts = [0, 4, 1000, WINDOW_CAP - 1, WINDOW_CAP, WINDOW_CAP + 1, 2 * GiB + 3 * step + 4,
+             3 * GiB - 7, 8 * GiB, 128 * GiB - 64, 128 * GiB + 64, 200 * GiB, 300 * GiB]
+    for left in lefts:
+        # enough windows to cross the cap and walk past the end where that is
+        # within reach, else a few thousand capped ones
+        cross = max(0, (left - WINDOW_CAP) // step + 1)
+        n = int(min(cross + 4 + (WINDOW_CAP // step + 2 if cross < 4000 else 0), 6000))
+        assert pg.sgemm_window_ranges(left, step, n) == expected_ranges(left, step, n), left
+
+
+def test_window_ranges_rejects_bad_arguments(pg):
+    with pytest.raises(pg.SgemmError):
+        pg.sgemm_window_ranges(100, 0, 3)
+    with pytest.raises(pg.SgemmError):
+        pg.sgemm_window_ranges(100, 64, -1)
+
+
 FAKE = 1 << 20  # never dereferenced: every call below returns before any device work
 
 
@@ -88,8 +120,6 @@ def call(pg, **over):
     (dict(strideA=-4), -15), (dict(strideB=-4), -16), (dict(strideC=-4), -17),
     # stored row length depends on the transpose flags
     (dict(transA=1, M=8, lda=4), -8), (dict(transB=1, K=8, ldb=4, lda=8), -10),
-    # leading dimensions at or above 2^21 are refused
-    (dict(lda=1 << 21), -8), (dict(ldb=1 << 21), -10), (dict(ldc=1 << 21), -13),
 ])
 def test_argument_errors(pg, over, status):
     assert call(pg, **over) == status
@@ -116,6 +146,25 @@ def test_variant_argument_checked(pg):
                                           4, 1, 0, 0, 0, pg.VARIANT_S64x64, check=False)
     assert st == -18  # 4-float variant forced on an unaligned A
     assert a  # keep the helper in use
+
+
+def test_any_leading_dimension_is_accepted(pg):
+    """Every ld at or above the stored row length is valid; a variant with
+    32-bit in-tile offsets cannot be forced for one of 2^21 or more (the
+    64-bit-addressed W64x64 builds run those calls). Nothing here launches."""
+    top = (1 << 31) - 1
+    assert call(pg, M=0, lda=top, ldb=top, ldc=top) == 0
+    assert call(pg, K=0, beta=1.0, lda=top) == 0
+    for which in ("lda", "ldb", "ldc"):
+        ld = dict(lda=4, ldb=4, ldc=4)
+        ld[which] = 1 << 21
+        for v in (pg.VARIANT_M128x128, pg.VARIANT_S64x64, pg.VARIANT_S64x64_V1,
+                  pg.VARIANT_T64x64, pg.VARIANT_T32x64, pg.VARIANT_S64x64_K2):
+            st = pg.sgemm_strided_batched_variant(0, 0, 4, 4, 4, 1.0, FAKE, ld["lda"], FAKE,
+                                                  ld["ldb"], 0.0, FAKE, ld["ldc"], 1, 0, 0, 0,
+                                                  v, check=False)
+            assert st == -18, (which, v)
+    assert "2^21" in pg.sgemm_status_string(-18)
 
 
 def test_status_strings(pg):

@@ -188,9 +188,9 @@ def canonical_vectors(tA, tB, M, N, K, lda, ldb):
     untransposed, ldb == 1; op(A) with M == 1, A transposed, lda == 1) is
     described k-contiguous, the same memory, as the library does before it
     picks the load width."""
-    if N == 1 and tB == 0 and ldb == 1 and 1 < K < 1 << 21:
+    if N == 1 and tB == 0 and ldb == 1 and 1 < K:
         tB, ldb = 1, K
-    if M == 1 and tA == 1 and lda == 1 and 1 < K < 1 << 21:
+    if M == 1 and tA == 1 and lda == 1 and 1 < K:
         tA, lda = 0, K
     return tA, tB, lda, ldb
 
@@ -219,7 +219,7 @@ def test_integer_sweep_bitwise(env, variant):
                          lda=(M if tA else K) + pad, ldb=(K if tB else N) + pad, ldc=N + pad)
             A, B, C = workloads.make_inputs(w)
             st, got = run_gpu(env, w, A, B, C, variant=variant)
-            if pg.VARIANT_NAMES[variant] != "S64x64_V1" and not vec4_possible(w):
+            if not pg.VARIANT_NAMES[variant].endswith("_V1") and not vec4_possible(w):
                 assert st == -18, (w, st)
                 continue
             assert st == 0, (w, st)
@@ -243,7 +243,7 @@ def test_float_sweep_bound(env, variant):
                         "stride_c": w.SC + 20})
         A, B, C = workloads.make_inputs(w)
         st, got = run_gpu(env, w, A, B, C, variant=variant)
-        if variant != 3 and not vec4_possible(w):
+        if not pg_constants.VARIANT_NAMES[variant].endswith("_V1") and not vec4_possible(w):
             assert st == -18
             continue
         assert st == 0, (w, st)
@@ -562,7 +562,7 @@ def test_batch_beyond_one_launch(env, tA, tB, M, N):
 
 @pytest.mark.parametrize("which", ["lda", "ldb", "ldc"])
 def test_leading_dimension_at_the_limit(env, which):
-    """Leading dimensions at 2^21 - 1, the largest the header allows."""
+    """Leading dimensions at 2^21 - 1, the largest the 32-bit-offset kernels take."""
     big = (1 << 21) - 1
     kw = {which: big}
     w = Workload("bigld", 0, 0, 5, 7, 9, 1.5, 0.5, seed=22, **kw)

@@ -74,3 +74,15 @@ def test_bench_roofline_bound_follows_the_ridge():
     assert (e["bound"], e["unit"], e["traffic"]) == ("mfma", "TFLOP/s", 123)
     assert e["achieved"] == pytest.approx(tflops, abs=1e-3)
     assert e["hbm_frac_at_achieved"] == pytest.approx(e["hbm_gbs_at_achieved"] / 8000.0, abs=1e-4)
+    # the skinny product is reported against HBM from its HBM-resident time,
+    # with its MFMA fraction beside it
+    sk = workloads.BY_NAME["skinny_16384x64x4096_nt"]
+    roof = measure.place_on_roofline(sk.flops(), sk.algorithmic_bytes(), peak, bw)
+    assert roof.bound == "compute-bound"
+    ms = 0.1
+    tflops = sk.flops() / (ms * 1e-3) / 1e12
+    e = bench.roofline_entry(sk, roof, tflops, peak / 1e12, ms, None, hbm_figure=True)
+    assert (e["bound"], e["unit"], e["timing"]) == ("hbm", "GB/s", "hbm_resident")
+    assert e["achieved"] == pytest.approx(277_872_640 / 1e-4 / 1e9, rel=1e-4)
+    assert e["mfma_frac_at_achieved"] == pytest.approx(tflops / 157.3, abs=1e-4)
+    assert "skinny_16384x64x4096_nt" in bench.HBM_FIGURE
