@@ -312,6 +312,37 @@ int sgemm_colmajor_strided_batched(int transA, int transB, int M, int N, int K,
                                    sgemm_stream_t stream);
 
 /*
+ * sgemm_strided_batched_ws_variant's automatic-variant call that allocates
+ * nothing and takes no workspace: for callers that cannot call hipMalloc
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation). The split-K partial tiles go to a fixed array of
+ * SGEMM_NOALLOC_SCRATCH_BYTES in device memory that the library holds on
+ * every GPU it runs on until the process ends (hipGetSymbolAddress finds its
+ * address once per device, on the first call made with that device
+ * current). splits: 0 = the automatic split, with no more slices than the
+ * array holds; 1 = no split; S >= 2 = forced as in
+ * sgemm_strided_batched_ws_variant, refused with -23 when S slices of
+ * 4 * M * N * batch bytes exceed the array (nothing is launched then).
+ * Results are bit for bit those of sgemm_strided_batched_ws_variant with
+ * SGEMM_VARIANT_AUTO, the same split count and a workspace of
+ * SGEMM_NOALLOC_SCRATCH_BYTES. The caller still owns and passes A, B and C.
+ * All calls on one GPU share its array and nothing in it is cleared or needs
+ * to be: calls that overlap on one GPU (other streams, other host threads)
+ * race and must be serialised by the caller. Status codes as
+ * sgemm_strided_batched_ws_variant, plus -19 for a split count below 0 or
+ * over 65535 and -23 as above.
+ */
+#define SGEMM_NOALLOC_SCRATCH_BYTES (32u << 20)
+
+int sgemm_strided_batched_noalloc(int transA, int transB, int M, int N, int K,
+                                  float alpha, const float *A, int lda,
+                                               const float *B, int ldb,
+                                  float beta,        float *C, int ldc,
+                                  int batch, long long strideA, long long strideB,
+                                  long long strideC, int splits,
+                                  sgemm_stream_t stream);
+
+/*
  * Host-side check of the buffer-range bookkeeping the tile and streaming
  * kernels use while their load window walks an operand (tests; no device
  * call). A window starts `left_bytes` before the end of the operand and moves

@@ -19,7 +19,8 @@ __all__ = [
     "sgemm_batched", "sgemm_batched_variant", "sgemm_colmajor",
     "sgemm_colmajor_strided_batched", "pointer_array", "sgemm_ws", "sgemm_strided_batched_ws",
     "sgemm_strided_batched_ws_variant", "sgemm_workspace_size", "sgemm_select_splits",
-    "sgemm_status_string", "sgemm_select_variant", "sgemm_window_ranges", "matmul",
+    "sgemm_status_string", "sgemm_select_variant", "sgemm_window_ranges",
+    "sgemm_strided_batched_noalloc", "NOALLOC_SCRATCH_BYTES", "matmul",
     "library_path",
     "VARIANT_AUTO", "VARIANT_L256x128", "VARIANT_M128x128", "VARIANT_S64x64",
     "VARIANT_S64x64_V1", "VARIANT_T64x64", "VARIANT_L256x256", "VARIANT_S64x64_K2",
@@ -45,6 +46,10 @@ VARIANT_COUNT = 13
 VARIANT_NAMES = {0: "L256x128", 1: "M128x128", 2: "S64x64", 3: "S64x64_V1", 4: "T64x64",
                  5: "L256x256", 6: "S64x64_K2", 7: "M128x128_DMA",
                  8: "T32x64", 9: "T64x32", 10: "GEMV", 11: "W64x64", 12: "W64x64_V1"}
+
+# SGEMM_NOALLOC_SCRATCH_BYTES of the C header: the fixed device array of the
+# entry point that allocates nothing
+NOALLOC_SCRATCH_BYTES = 32 << 20
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _lib = None
@@ -106,6 +111,9 @@ def _load():
     lib.sgemm_colmajor_strided_batched.restype = i
     lib.sgemm_colmajor_strided_batched.argtypes = [i, i, i, i, i, f, p, i, p, i, f, p, i, i,
                                                    ll, ll, ll, p]
+    lib.sgemm_strided_batched_noalloc.restype = i
+    lib.sgemm_strided_batched_noalloc.argtypes = [i, i, i, i, i, f, p, i, p, i, f, p, i, i, ll,
+                                                  ll, ll, i, p]
     lib.sgemm_window_ranges.restype = i
     lib.sgemm_window_ranges.argtypes = [ll, i, i, ctypes.POINTER(ctypes.c_uint)]
     _lib = lib
@@ -244,6 +252,18 @@ def sgemm_strided_batched_ws_variant(transA, transB, M, N, K, alpha, A, lda, B, 
         int(transA), int(transB), M, N, K, float(alpha), _ptr(A), lda, _ptr(B), ldb,
         float(beta), _ptr(C), ldc, batch, strideA, strideB, strideC, int(variant), int(splits),
         wp, wb, _stream(stream, A, B, C))
+    return _check(st, check)
+
+
+def sgemm_strided_batched_noalloc(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
+                                  batch, strideA, strideB, strideC, splits=0, stream=None,
+                                  check=True) -> int:
+    """C ABI ``sgemm_strided_batched_noalloc`` (split-K partials in the
+    library's fixed device array; allocates nothing)."""
+    st = _load().sgemm_strided_batched_noalloc(
+        int(transA), int(transB), M, N, K, float(alpha), _ptr(A), lda, _ptr(B), ldb,
+        float(beta), _ptr(C), ldc, batch, strideA, strideB, strideC, int(splits),
+        _stream(stream, A, B, C))
     return _check(st, check)
 
 

@@ -52,6 +52,7 @@
 #include <hip/hip_runtime.h>
 
 #include <atomic>
+#include <mutex>
 #include <type_traits>
 #include <stdint.h>
 
@@ -2416,6 +2417,76 @@ extern "C" int sgemm_window_ranges(long long left_bytes, int step_bytes, int nst
     return 0;
 }
 
+// ---------------------------------------------------------------------------
+// The entry point that allocates nothing: the split-K partial tiles go to a
+// fixed device-resident array instead of a caller workspace. Each GPU the
+// library runs on holds its own copy of it until the process ends. Host code
+// never uses the array's name as an address (on the host it is only a
+// stand-in): the device address comes from hipGetSymbolAddress, once per
+// device with that device current, and that pointer is what the kernels get.
+// Every partial element the reduction reads is written first by the tile
+// kernel of the same call, so nothing in the array needs clearing; calls
+// that overlap on one GPU share the array and race.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) float scratch[SGEMM_NOALLOC_SCRATCH_BYTES / sizeof(float)];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+float *g_scratch_ptr[kMaxDevices];
+int g_scratch_status[kMaxDevices];
+
+// Device address of this device's scratch array (0 on success).
+int scratch_of_current_device(float **out)
+{
+    int dev = 0;
+    const hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return (int)e;
+    if (dev < 0 || dev >= kMaxDevices)
+        return (int)hipErrorInvalidDevice;
+    std::call_once(g_scratch_once[dev], [dev] {
+        void *ptr = nullptr;
+        const hipError_t r = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        g_scratch_status[dev] = (int)r;
+        g_scratch_ptr[dev] = r == hipSuccess ? static_cast<float *>(ptr) : nullptr;
+    });
+    if (g_scratch_status[dev] != 0)
+        return g_scratch_status[dev];
+    *out = g_scratch_ptr[dev];
+    return 0;
+}
+
+} // namespace
+
+extern "C" int sgemm_strided_batched_noalloc(int transA, int transB, int M, int N, int K,
+                                             float alpha, const float *A, int lda,
+                                             const float *B, int ldb, float beta, float *C,
+                                             int ldc, int batch, long long strideA,
+                                             long long strideB, long long strideC, int splits,
+                                             sgemm_stream_t stream)
+{
+    const int st = validate(transA, transB, M, N, K, A, lda, B, ldb, C, ldc, batch, strideA,
+                            strideB, strideC, alpha, beta);
+    if (st != 0)
+        return st;
+    if (splits < 0 || splits > 65535)
+        return -19;
+    float *ws = nullptr;
+    const int se = scratch_of_current_device(&ws);
+    if (se != 0)
+        return se;
+    const Call c{transA, transB, M, N, K, alpha, beta, A, B, C, lda, ldb, ldc, batch,
+                 strideA, strideB, strideC, nullptr, nullptr, nullptr};
+    const Split sk{ws, SGEMM_NOALLOC_SCRATCH_BYTES, splits};
+    // A forced split whose partial tiles would not fit the array is refused
+    // before anything is launched (-21 from the launch path, reported as
+    // -23); the automatic choice takes no more slices than fit.
+    const int r = launch(c, SGEMM_VARIANT_AUTO, reinterpret_cast<hipStream_t>(stream), sk);
+    return r == -21 ? -23 : r;
+}
+
 extern "C" const char *sgemm_status_string(int status)
 {
     switch (status) {
@@ -2440,6 +2511,7 @@ extern "C" const char *sgemm_status_string(int status)
     case -20: return "invalid workspace (NULL or not 4-byte aligned while workspace_bytes > 0)";
     case -21: return "workspace too small for the requested split count";
     case -22: return "problem too large: one batch item has more output tiles than one launch holds";
+    case -23: return "split too large: its partial tiles exceed the fixed scratch of the no-allocation entry point (SGEMM_NOALLOC_SCRATCH_BYTES)";
     default: break;
     }
     if (status < 0)
