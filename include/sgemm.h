@@ -133,7 +133,15 @@ enum sgemm_variant {
                                     offsets: any leading dimension (chosen for calls with
                                     an ld of 2^21 or more) */
     SGEMM_VARIANT_W64x64_V1 = 12,/* the same with 1-float loads (any alignment) */
-    SGEMM_VARIANT_COUNT = 13
+    SGEMM_VARIANT_P128x128 = 13,/* persistent: one 12-wave workgroup per compute unit, three
+                                    groups of 4 waves each on 128 x 128 tiles; the unit's
+                                    n = 3q + 1 tiles go q whole to each group and the last
+                                    one split over K into thirds, summed in LDS. Needs the
+                                    tiles (times batch) to split evenly over the compute
+                                    units with n % 3 != 2, and K >= 192 when n % 3 == 1;
+                                    strided calls only, no split-K (-18 / -19 otherwise) */
+    SGEMM_VARIANT_P64x64 = 14,  /*  the same on 64 x 64 tiles */
+    SGEMM_VARIANT_COUNT = 15
 };
 
 /*

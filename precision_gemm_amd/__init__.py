@@ -25,7 +25,8 @@ __all__ = [
     "VARIANT_AUTO", "VARIANT_L256x128", "VARIANT_M128x128", "VARIANT_S64x64",
     "VARIANT_S64x64_V1", "VARIANT_T64x64", "VARIANT_L256x256", "VARIANT_S64x64_K2",
     "VARIANT_M128x128_DMA", "VARIANT_T32x64", "VARIANT_T64x32", "VARIANT_GEMV",
-    "VARIANT_W64x64", "VARIANT_W64x64_V1", "VARIANT_COUNT", "VARIANT_NAMES",
+    "VARIANT_W64x64", "VARIANT_W64x64_V1", "VARIANT_P128x128", "VARIANT_P64x64",
+    "VARIANT_COUNT", "VARIANT_NAMES",
 ]
 
 VARIANT_AUTO = -1
@@ -42,10 +43,13 @@ VARIANT_T64x32 = 9
 VARIANT_GEMV = 10
 VARIANT_W64x64 = 11
 VARIANT_W64x64_V1 = 12
-VARIANT_COUNT = 13
+VARIANT_P128x128 = 13
+VARIANT_P64x64 = 14
+VARIANT_COUNT = 15
 VARIANT_NAMES = {0: "L256x128", 1: "M128x128", 2: "S64x64", 3: "S64x64_V1", 4: "T64x64",
                  5: "L256x256", 6: "S64x64_K2", 7: "M128x128_DMA",
-                 8: "T32x64", 9: "T64x32", 10: "GEMV", 11: "W64x64", 12: "W64x64_V1"}
+                 8: "T32x64", 9: "T64x32", 10: "GEMV", 11: "W64x64", 12: "W64x64_V1",
+                 13: "P128x128", 14: "P64x64"}
 
 # SGEMM_NOALLOC_SCRATCH_BYTES of the C header: the fixed device array of the
 # entry point that allocates nothing

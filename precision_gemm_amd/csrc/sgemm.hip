@@ -94,6 +94,9 @@ struct Params {
     // GEMV kernels only: the first output row of this launch (a launch covers
     // at most 2^31 - 1 work-items, so a very tall matrix takes several).
     int row_base;
+    // Persistent kernel only: output tiles per workgroup (one workgroup per
+    // compute unit; tiles_m * tiles_n * batch = slot_tiles * workgroups).
+    int slot_tiles;
 };
 
 __device__ __forceinline__ const float *item_a(const Params &p, int b)
@@ -181,6 +184,10 @@ __device__ __forceinline__ float global_load1(const float *q)
 {
     return *(const __attribute__((address_space(1))) float *)q;
 }
+
+// s_waitcnt immediate that waits for vmcnt <= n only (gfx9 encoding: vmcnt in
+// bits 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at their maxima).
+constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const float *base, long long elems)
 {
@@ -372,15 +379,10 @@ struct Operand {
     }
 };
 
-// Flat workgroup id -> (batch item, tile row, tile column).
-__device__ __forceinline__ void tile_of(const Params &p, int &b, int &tm, int &tn)
+// Logical tile index -> (batch item, tile row, tile column): items one after
+// another, each in grouped order.
+__device__ __forceinline__ void decode_tile(const Params &p, int logical, int &b, int &tm, int &tn)
 {
-    const int num = gridDim.x * gridDim.y;
-    const int pid = blockIdx.y * gridDim.x + blockIdx.x;
-    // Workgroup pid runs on XCD pid % 8; give each XCD a contiguous range.
-    const int xcd = pid % kNumXcd, local = pid / kNumXcd;
-    const int q = num / kNumXcd, r = num % kNumXcd;
-    const int logical = xcd < r ? xcd * (q + 1) + local : r * (q + 1) + (xcd - r) * q + local;
     const int per_batch = p.tiles_m * p.tiles_n;
     b = logical / per_batch;
     const int t = logical % per_batch;
@@ -390,6 +392,18 @@ __device__ __forceinline__ void tile_of(const Params &p, int &b, int &tm, int &t
     const int gsize = min(p.tiles_m - first_m, p.group_m);
     tm = first_m + (t % in_group) % gsize;
     tn = (t % in_group) / gsize;
+}
+
+// Flat workgroup id -> (batch item, tile row, tile column).
+__device__ __forceinline__ void tile_of(const Params &p, int &b, int &tm, int &tn)
+{
+    const int num = gridDim.x * gridDim.y;
+    const int pid = blockIdx.y * gridDim.x + blockIdx.x;
+    // Workgroup pid runs on XCD pid % 8; give each XCD a contiguous range.
+    const int xcd = pid % kNumXcd, local = pid / kNumXcd;
+    const int q = num / kNumXcd, r = num % kNumXcd;
+    const int logical = xcd < r ? xcd * (q + 1) + local : r * (q + 1) + (xcd - r) * q + local;
+    decode_tile(p, logical, b, tm, tn);
 }
 
 // Epilogue of a tile kernel: C = alpha * res + beta * C for this wave's
@@ -699,6 +713,227 @@ sgemm_mfma_kernel(Params p)
 }
 
 // ---------------------------------------------------------------------------
+// Persistent tile kernel: one workgroup per compute unit, looping over that
+// unit's output tiles, the pattern "Triton Optimization Reference (cuTile ->
+// Triton)" describes for persistent kernels (a grid sized to the machine,
+// each program walking tiles in grouped order). The workgroup is twelve
+// waves, three groups of 2 x 2 waves that each own a BM x BN accumulator, so
+// every SIMD runs three waves as with three workgroups per CU. A unit with n
+// tiles, n = 3q + 1, gives each group q whole tiles and then a third of the K
+// range of the last one (the stream-K split of a ragged last round, kept
+// inside the CU): the three partial tiles are added in LDS in a fixed order,
+// (group 0 + group 1) + group 2, so results do not depend on timing. Every
+// group runs the same number of K-steps in every tile, so the workgroup-wide
+// barriers of the K loop line up by construction: no group ever waits at a
+// barrier the others do not reach. A third of K is a piece of L_g k (L_1 =
+// L_2 = K/3 rounded up to a multiple of 4, L_0 the rest), all run as the same
+// number of 16-deep steps P: a piece's first window starts L_g - 16P before
+// its end (up to 31 k before its start), and the first two loads of every
+// tile mask k outside [0, L_g). Tiles on one XCD (workgroup pid runs on XCD
+// pid % 8) are a contiguous range of the grouped order, and the groups of the
+// XCD's workgroups take consecutive tiles of it at the same time.
+// ---------------------------------------------------------------------------
+template <int BM, int BN, bool A_KC, bool B_KC>
+__global__ void __attribute__((amdgpu_flat_work_group_size(768, 768), amdgpu_waves_per_eu(3)))
+sgemm_persistent_kernel(Params p)
+{
+    constexpr int BK = 16, NT = 256, GROUPS = 3;
+    constexpr int WM = BM / 2, WN = BN / 2, TM = WM / 32, TN = WN / 32;
+    constexpr int NQ = BK / 8, LATE = TM * TN;
+    using OpA = Operand<A_KC, BM, BK, NT, 4>;
+    using OpB = Operand<B_KC, BN, BK, NT, 4>;
+    constexpr int STAGE = OpA::STAGE + OpB::STAGE;
+    constexpr int PART = 4 * TM * TN * 16 * 64; // one group's accumulators
+    constexpr int LDS = GROUPS * 2 * STAGE > 2 * PART ? GROUPS * 2 * STAGE : 2 * PART;
+    __shared__ __attribute__((aligned(16))) float lds[LDS];
+
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int grp = wave / 4, wg = wave % 4;
+    const int wm0 = (wg % 2) * WM, wn0 = (wg / 2) * WN;
+    float *stages = lds + grp * 2 * STAGE;
+
+    // This workgroup's tiles: XCD x owns the logical tiles
+    // [x * per_xcd, (x + 1) * per_xcd); its workgroup l takes, in round u,
+    // local tile (3u + g) * slots_x + l for group g, and the split tile
+    // 3q * slots_x + l.
+    const int pid = blockIdx.x, slots = gridDim.x;
+    const int slots_x = slots / kNumXcd, xcd = pid % kNumXcd, l = pid / kNumXcd;
+    const int n = p.slot_tiles, q = n / 3;
+    const int first = xcd * slots_x * n;
+
+    const int K = p.K;
+    const int steps_whole = (K + BK - 1) / BK;
+    const int piece = 4 * ((K + 11) / 12);           // L_1 = L_2
+    const int my_k0 = grp == 0 ? 0 : K - (GROUPS - grp) * piece;
+    const int my_len = grp == 0 ? K - 2 * piece : piece;
+    const int steps_piece = (piece + BK - 1) / BK;   // P (L_0 <= L_1)
+
+    f32x16 acc[TM][TN];
+    // One tile: the product of op(A)[m0.., k0..k0+len) and op(B)[k0..k0+len,
+    // n0..) over `steps` K-steps into acc (cleared first).
+    auto run_unit = [&](int lane, int b, int m0, int n0, int k0, int len, int steps) {
+        const int tid = wg * 64 + lane;
+        const float *Ab = item_a(p, b) + (A_KC ? (long long)k0 : (long long)k0 * p.lda);
+        const float *Bb = item_b(p, b) + (B_KC ? (long long)k0 : (long long)k0 * p.ldb);
+        OpA opa;
+        opa.X = Ab;
+        opa.ld = p.lda;
+        opa.total = A_KC ? (long long)(p.M - 1) * p.lda + len : (long long)(len - 1) * p.lda + p.M;
+        opa.O = p.M;
+        opa.K = len;
+        opa.o0 = m0;
+        const int kfirst = len - BK * steps;
+        opa.init(tid, kfirst);
+        OpB opb;
+        opb.X = Bb;
+        opb.ld = p.ldb;
+        opb.total = B_KC ? (long long)(p.N - 1) * p.ldb + len : (long long)(len - 1) * p.ldb + p.N;
+        opb.O = p.N;
+        opb.K = len;
+        opb.o0 = n0;
+        opb.init(tid, kfirst);
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+                acc[i][j] = f32x16{};
+        f32x4 ra[OpA::SLOTS], rb[OpB::SLOTS];
+        using Masked = std::true_type;
+        using Full = std::false_type;
+        auto load = [&](auto tail) {
+            opa.template load_next<decltype(tail)::value>(tid, ra);
+            opb.template load_next<decltype(tail)::value>(tid, rb);
+        };
+        auto read_group = [&](const float *stage, int qq, float (&fa)[TM][4], float (&fb)[TN][4]) {
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+                OpA::frag(stage, wm0 + 32 * i, qq, lane, fa[i]);
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+                OpB::frag(stage + OpA::STAGE, wn0 + 32 * j, qq, lane, fb[j]);
+        };
+        auto mfma_group = [&](const float (&fa)[TM][4], const float (&fb)[TN][4], int lo, int hi) {
+#pragma unroll
+            for (int t = 0; t < 4 * TM * TN; ++t) {
+                if (t < lo || t >= hi)
+                    continue;
+                const int kk = t / (TM * TN), i = (t / TN) % TM, j = t % TN;
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[i][kk], fb[j][kk], acc[i][j],
+                                                                  0, 0, 0);
+            }
+        };
+        // Both prologue loads mask k outside [0, len): a piece's first window
+        // may start up to 31 k before it.
+        load(Masked{});
+        OpA::store(stages, tid, ra);
+        OpB::store(stages + OpA::STAGE, tid, rb);
+        load(Masked{});
+        __syncthreads();
+        float fa[NQ][TM][4], fb[NQ][TN][4];
+        read_group(stages, 0, fa[0], fb[0]);
+        auto k_step = [&](auto parity) {
+            constexpr int PAR = decltype(parity)::value;
+            const float *cur = stages + PAR * STAGE;
+            float *nxt = stages + (1 - PAR) * STAGE;
+#pragma unroll
+            for (int qq = 1; qq < NQ; ++qq)
+                read_group(cur, qq, fa[qq], fb[qq]);
+            mfma_group(fa[0], fb[0], 0, 4 * TM * TN);
+            OpA::store(nxt, tid, ra);
+            OpB::store(nxt + OpA::STAGE, tid, rb);
+            load(Full{});
+#pragma unroll
+            for (int qq = 1; qq < NQ - 1; ++qq)
+                mfma_group(fa[qq], fb[qq], 0, 4 * TM * TN);
+            mfma_group(fa[NQ - 1], fb[NQ - 1], 0, 4 * TM * TN - LATE);
+            __builtin_amdgcn_sched_group_barrier(0x100, 4 * (TM + TN) * (NQ - 1), 0);
+#pragma unroll
+            for (int w = 0; w < OpA::SLOTS + OpB::SLOTS; ++w) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0); // MFMA
+                __builtin_amdgcn_sched_group_barrier(0x200, 1, 0); // LDS write
+            }
+#pragma unroll
+            for (int w = 0; w < OpA::SLOTS + OpB::SLOTS; ++w) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0); // MFMA
+                __builtin_amdgcn_sched_group_barrier(0x020, 1, 0); // global load
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            __syncthreads();
+            __builtin_amdgcn_sched_barrier(0);
+            read_group(nxt, 0, fa[0], fb[0]);
+            mfma_group(fa[NQ - 1], fb[NQ - 1], 4 * TM * TN - LATE, 4 * TM * TN);
+            __builtin_amdgcn_sched_group_barrier(0x100, 4 * (TM + TN), 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, LATE, 0);
+        };
+        using P0 = std::integral_constant<int, 0>;
+        using P1 = std::integral_constant<int, 1>;
+        int s = 0;
+        for (; s + 1 < steps; s += 2) {
+            k_step(P0{});
+            k_step(P1{});
+        }
+        if (s < steps)
+            k_step(P0{});
+    };
+
+    // Tiles: q whole ones, then (n % 3 == 1) this group's third of the split
+    // tile. The split tile is the same for the whole workgroup, so the
+    // barriers of its exchange are reached by every wave.
+    const int units = q + (n - 3 * q == 1 ? 1 : 0);
+    for (int u = 0; u < units; ++u) {
+        // The lane index, opaque to the compiler in every tile: the per-lane
+        // load, LDS and store offsets are then recomputed per tile instead of
+        // hoisted out of this loop and held (spilled) across the K loop.
+        int lane = threadIdx.x & 63;
+        asm volatile("" : "+v"(lane));
+        const bool split = u == q;
+        int b, tm, tn;
+        decode_tile(p, first + (split ? 3 * q : 3 * u + grp) * slots_x + l, b, tm, tn);
+        run_unit(lane, b, tm * BM, tn * BN, split ? my_k0 : 0, split ? my_len : K,
+                 split ? steps_piece : steps_whole);
+        if (split) {
+            // Groups 0 and 1 hand their partial tiles to group 2, which adds
+            // (group 0 + group 1) + its own and stores the tile.
+            auto xidx = [&](int g, int i, int j, int v) {
+                return ((((g * 4 + wg) * TM + i) * TN + j) * 16 + v) * 64 + lane;
+            };
+            __syncthreads(); // every wave is past its last read of the stages
+            if (grp < 2) {
+#pragma unroll
+                for (int i = 0; i < TM; ++i)
+#pragma unroll
+                    for (int j = 0; j < TN; ++j)
+#pragma unroll
+                        for (int v = 0; v < 16; ++v)
+                            lds[xidx(grp, i, j, v)] = acc[i][j][v];
+            }
+            __syncthreads();
+            if (grp == 2) {
+#pragma unroll
+                for (int i = 0; i < TM; ++i)
+#pragma unroll
+                    for (int j = 0; j < TN; ++j)
+#pragma unroll
+                        for (int v = 0; v < 16; ++v)
+                            acc[i][j][v] = (lds[xidx(0, i, j, v)] + lds[xidx(1, i, j, v)]) +
+                                           acc[i][j][v];
+            }
+        }
+        if (!split || grp == 2) {
+            float res[TM][TN][16];
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+#pragma unroll
+                    for (int v = 0; v < 16; ++v)
+                        res[i][j][v] = acc[i][j][v];
+            store_tile<TM, TN, 16>(p, item_c(p, b), tm * BM, tn * BN, wm0, wn0, 0, lane, res);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Streaming kernel for grids of few tiles over a deep K (never launched with
 // split-K): a BM x 64 tile per workgroup whose WAVES waves each own every
 // WAVES-th K-step (wave w takes steps w, w+WAVES, ...) and accumulate the
@@ -818,10 +1053,6 @@ struct DmaOperand {
         }
     }
 };
-
-// s_waitcnt immediate that waits for vmcnt <= n only (gfx9 encoding: vmcnt in
-// bits 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at their maxima).
-constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
 // Wait until at most min(n, MAXN) groups of NI vector-memory operations are in
 // flight (n < 0: none). n is wave-uniform; each case has its own immediate.
@@ -1571,6 +1802,16 @@ constexpr VariantInfo make_dma_variant()
                          sgemm_dma_kernel<BM, BN, WM_, WN_, MW, false, true>}}};
 }
 
+template <int BM, int BN>
+constexpr VariantInfo make_persistent_variant()
+{
+    return VariantInfo{BM, BN, 16, 768, 4,
+                       {{sgemm_persistent_kernel<BM, BN, true, false>,
+                         sgemm_persistent_kernel<BM, BN, true, true>},
+                        {sgemm_persistent_kernel<BM, BN, false, false>,
+                         sgemm_persistent_kernel<BM, BN, false, true>}}};
+}
+
 template <int WAVES, int STAGES, int BM, int BN, int MINW>
 constexpr VariantInfo make_stream_variant()
 {
@@ -1597,7 +1838,32 @@ const VariantInfo kVariants[SGEMM_VARIANT_COUNT] = {
     VariantInfo{4, 1, 4, 256, 4, {{nullptr, sgemv_kernel<4>}, {nullptr, sgemv_t_kernel<64>}}},
     make_variant<64, 64, kBK, 2, 2, 1, 4, 4, true>(), // SGEMM_VARIANT_W64x64
     make_variant<64, 64, kBK, 2, 2, 1, 4, 1, true>(), // SGEMM_VARIANT_W64x64_V1
+    make_persistent_variant<128, 128>(),              // SGEMM_VARIANT_P128x128
+    make_persistent_variant<64, 64>(),                // SGEMM_VARIANT_P64x64
 };
+
+bool is_persistent(int variant)
+{
+    return variant == SGEMM_VARIANT_P128x128 || variant == SGEMM_VARIANT_P64x64;
+}
+
+// Tiles per workgroup of the persistent kernel for this grid on `cus`
+// compute units (one workgroup each), or 0 when it cannot run it: the tiles
+// must split evenly over the workgroups, eight XCDs apart, into n per
+// workgroup with n % 3 != 2 (its three wave groups then take whole tiles, or
+// whole tiles and a third of the K range of one more each, which needs
+// K >= 192 so that every third is at least four K-steps).
+long long persistent_tiles(int variant, int M, int N, int K, int batch, long long cus)
+{
+    const VariantInfo &vi = kVariants[variant];
+    const long long tiles = ((long long)M + vi.bm - 1) / vi.bm * (((long long)N + vi.bn - 1) / vi.bn) * batch;
+    if (cus < 8 || cus % 8 != 0 || tiles % cus != 0 || tiles / cus > INT32_MAX || tiles > INT32_MAX)
+        return 0;
+    const long long n = tiles / cus;
+    if (n % 3 == 2 || (n % 3 == 1 && K < 192))
+        return 0;
+    return n;
+}
 
 // The 64-bit-addressed builds, which take any leading dimension.
 bool is_wide(int variant)
@@ -1616,7 +1882,10 @@ bool is_stream(int variant)
 }
 
 // Variants that never split K across workgroups.
-bool no_split(int variant) { return is_stream(variant) || variant == SGEMM_VARIANT_GEMV; }
+bool no_split(int variant)
+{
+    return is_stream(variant) || variant == SGEMM_VARIANT_GEMV || is_persistent(variant);
+}
 
 int num_cus_of_current_device(int *out)
 {
@@ -2027,7 +2296,7 @@ int launch_canonical(const Call &c, int variant, hipStream_t s, Split sk)
         (b_kc ? c.K % 4 == 0 : c.N % 4 == 0);
     const bool auto_variant = variant == SGEMM_VARIANT_AUTO;
     int cus = 0;
-    if (auto_variant || sk.splits == 0) {
+    if (auto_variant || sk.splits == 0 || is_persistent(variant)) {
         const int st = num_cus_of_current_device(&cus);
         if (st != 0)
             return st;
@@ -2043,7 +2312,9 @@ int launch_canonical(const Call &c, int variant, hipStream_t s, Split sk)
         if (wide && variant != SGEMM_VARIANT_GEMV)
             variant = vec4_ok ? SGEMM_VARIANT_W64x64 : SGEMM_VARIANT_W64x64_V1;
     } else if ((kVariants[variant].vec == 4 && !vec4_ok) ||
-               (wide && !is_wide(variant) && variant != SGEMM_VARIANT_GEMV)) {
+               (wide && !is_wide(variant) && variant != SGEMM_VARIANT_GEMV) ||
+               (is_persistent(variant) &&
+                (arrays || persistent_tiles(variant, c.M, c.N, c.K, c.batch, cus) == 0))) {
         return -18;
     }
     if (variant == SGEMM_VARIANT_GEMV) {
@@ -2121,6 +2392,35 @@ int launch_canonical(const Call &c, int variant, hipStream_t s, Split sk)
             splits = (int)S;
             kslice = (int)ks;
         }
+    }
+
+    if (is_persistent(variant)) {
+        if (splits > 1)
+            return -19;
+        Params p{};
+        p.A = c.A;
+        p.B = c.B;
+        p.C = c.C;
+        p.M = c.M;
+        p.N = c.N;
+        p.K = c.K;
+        p.lda = c.lda;
+        p.ldb = c.ldb;
+        p.ldc = c.ldc;
+        p.sA = c.sA;
+        p.sB = c.sB;
+        p.sC = c.sC;
+        p.alpha = c.alpha;
+        p.beta = c.beta;
+        p.tiles_m = (int)ceil_div(c.M, kVariants[variant].bm);
+        p.tiles_n = (int)ceil_div(c.N, kVariants[variant].bn);
+        p.group_m = 8;
+        p.splits = 1;
+        p.kslice = c.K;
+        p.slot_tiles = (int)persistent_tiles(variant, c.M, c.N, c.K, c.batch, cus);
+        void *args[] = {&p};
+        return (int)hipLaunchKernel((const void *)kVariants[variant].fn[c.tA][c.tB],
+                                    dim3((unsigned)cus), dim3(768), args, 0, s);
     }
 
     const VariantInfo &vi = kVariants[variant];

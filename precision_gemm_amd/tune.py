@@ -144,7 +144,8 @@ def sweep(shapes, rounds: int = 3, target_ms: float = 20.0, out=sys.stdout):
                    (2 <= M <= 8 and cB == 1 and (cA == 0 or M % 4 == 0)))
         auto = pg.sgemm_select_variant(cA, cB, M, N, K, batch, 1, cus)
         variants = [v for v in range(pg.VARIANT_COUNT)
-                    if v not in (pg.VARIANT_S64x64_V1, pg.VARIANT_W64x64, pg.VARIANT_W64x64_V1)
+                    if v not in (pg.VARIANT_S64x64_V1, pg.VARIANT_W64x64, pg.VARIANT_W64x64_V1,
+                                 pg.VARIANT_P128x128, pg.VARIANT_P64x64)
                     and (v != pg.VARIANT_GEMV or gemv_ok)]
 
         def caller(v):

@@ -26,7 +26,11 @@ pytestmark = pytest.mark.gpu
 # every kernel variant that takes any shape (the enum of the C header,
 # mirrored by the binding); the GEMV kernel, which only takes N == 1 or M == 1,
 # has tests of its own
-ALL_VARIANTS = [v for v in range(pg_constants.VARIANT_COUNT) if v != pg_constants.VARIANT_GEMV]
+# (the persistent variants, which only take grids that split evenly over the
+# compute units, are tested in test_gpu_persistent.py)
+ALL_VARIANTS = [v for v in range(pg_constants.VARIANT_COUNT)
+                if v not in (pg_constants.VARIANT_GEMV, pg_constants.VARIANT_P128x128,
+                             pg_constants.VARIANT_P64x64)]
 
 GUARD = 64  # floats of canary before and after each device buffer (keeps 256-B alignment)
 
