@@ -20,9 +20,10 @@ copy's previous use have pushed out of L2 and the 256 MB Infinity Cache, so
 they come from HBM, while launches keep running back to back and the clock
 stays up. It gives the per-launch median, min and mean; for a workload whose
 figure of merit is its HBM rate (the skinny product and matrix-vector
-products) the roofline entry is taken from this mode. The GPU clock is sampled
-during both timed regions (``sclk_mhz``), and the run records the library file
-it loaded (path and hash) and the host CPU.
+products) the roofline entry is taken from this mode. The GPU clock
+while each mode's kernel ran is read from the committed counter pass
+(``sclk_mhz``: GRBM_GUI_ACTIVE over the kernel duration), and the run records
+the library file it loaded (path and hash) and the host CPU.
 
 Prints one JSON line. ``value`` is GFLOP/s (2*M*N*K per GEMM over the timed
 wall time). ``roofline`` reports the same kernel against the FP32-MFMA peak;
@@ -82,54 +83,6 @@ def host_info() -> dict:
     return {"cpu_model": model, "cores_available": cores}
 
 
-class ClockSampler:
-    """Samples the GPU's current graphics clock (MHz) every ~1 ms on a thread
-    while the context is open, through the AMD SMI library; reports the
-    samples' mean, min and max, or why it could not read them."""
-
-    def __init__(self):
-        self.samples, self.error, self._stop = [], None, None
-
-    def __enter__(self):
-        import threading
-        try:
-            import amdsmi
-            amdsmi.amdsmi_init(amdsmi.AmdSmiInitFlags.INIT_AMD_GPUS)
-            handle = amdsmi.amdsmi_get_processor_handles()[0]
-            self._read = lambda: amdsmi.amdsmi_get_clock_info(
-                handle, amdsmi.AmdSmiClkType.SYS)["clk"]
-            self._read()
-        except Exception as e:  # noqa: BLE001 -- report, never fail the bench
-            self.error = f"{type(e).__name__}: {e}"
-            return self
-        self._stop = threading.Event()
-
-        def loop():
-            while not self._stop.is_set():
-                try:
-                    self.samples.append(float(self._read()))
-                except Exception as e:  # noqa: BLE001
-                    self.error = f"{type(e).__name__}: {e}"
-                    return
-                self._stop.wait(0.001)
-        self._thread = threading.Thread(target=loop, daemon=True)
-        self._thread.start()
-        return self
-
-    def __exit__(self, *exc):
-        if self._stop is not None:
-            self._stop.set()
-            self._thread.join()
-        return False
-
-    def report(self):
-        if not self.samples:
-            return {"samples": 0, "error": self.error or "no samples"}
-        return {"samples": len(self.samples),
-                "mean": round(sum(self.samples) / len(self.samples), 1),
-                "min": min(self.samples), "max": max(self.samples)}
-
-
 def kernel_source_hash() -> str:
     """Hash of the device code of the kernel source (everything before its host
     section), comments and whitespace dropped: editing a comment or the host
@@ -146,19 +99,39 @@ def kernel_source_hash() -> str:
     return hashlib.sha256(" ".join(src.split()).encode()).hexdigest()[:16]
 
 
-def load_traffic(workload: str, variant: str):
-    """HBM bytes per launch from the committed counter summary, if it was
-    taken on the current kernel code and on the variant this run launches."""
+def counter_entry(workload: str, variant: str, mode: str = "back_to_back"):
+    """The committed counter summary of this workload in one timing mode
+    ("back_to_back" or "hbm_resident"), if it was taken on the current kernel
+    code and on the variant this run launches, else None."""
     try:
         with open(TRAFFIC_FILE) as f:
             data = json.load(f)
     except (OSError, ValueError):
         return None
-    entry = data.get(workload)
+    entry = data.get(workload if mode == "back_to_back" else f"{workload}@hbm")
     if (not entry or entry.get("kernel_sha") != kernel_source_hash()
             or entry.get("variant") != variant):
         return None
-    return entry.get("bytes_per_launch")
+    return entry
+
+
+def load_traffic(workload: str, variant: str, mode: str = "back_to_back"):
+    """HBM bytes per launch from the committed counter summary (see
+    counter_entry), else None."""
+    entry = counter_entry(workload, variant, mode)
+    return None if entry is None else entry.get("bytes_per_launch")
+
+
+def clock_report(workload: str, variant: str) -> dict:
+    """The GPU clock while the kernel ran, from the committed counter pass:
+    GRBM_GUI_ACTIVE (busy cycles of the graphics block, summed over the eight
+    XCDs) / 8 over the kernel's duration, per timing mode."""
+    out = {"source": "GRBM_GUI_ACTIVE / 8 / kernel duration in the committed rocprofv3 "
+                     "counter pass (profiles/traffic.json)"}
+    for mode in ("back_to_back", "hbm_resident"):
+        entry = counter_entry(workload, variant, mode)
+        out[mode] = None if entry is None else entry.get("sclk_mhz")
+    return out
 
 
 def cpu_baseline(w, A, B, C, got_c, target_s: float):
@@ -274,12 +247,11 @@ def hbm_resident(torch, dev, stream, w, dA, dB, dC, launch, steps, min_warmup_ms
             torch.cuda.synchronize(dev)
     torch.cuda.synchronize(dev)
     events = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
-    with ClockSampler() as clock:
-        events[0].record(stream)
-        for k in range(steps):
-            one(i + k)
-            events[k + 1].record(stream)
-        torch.cuda.synchronize(dev)
+    events[0].record(stream)
+    for k in range(steps):
+        one(i + k)
+        events[k + 1].record(stream)
+    torch.cuda.synchronize(dev)
     ms = [events[k].elapsed_time(events[k + 1]) for k in range(steps)]
     srt = sorted(ms)
     med, mean = srt[len(srt) // 2], sum(ms) / len(ms)
@@ -287,7 +259,8 @@ def hbm_resident(torch, dev, stream, w, dA, dB, dC, launch, steps, min_warmup_ms
     from precision_gemm_amd import measure
     del As, Bs, Cs
     return {
-        "copies": copies, "bytes_rotated": copies * per, "launches": steps,
+        "copies": copies, "bytes_rotated": copies * per, "warmup_launches": i,
+        "launches": steps,
         "mean_ms": round(mean, 5), "median_ms": round(med, 5), "min_ms": round(srt[0], 5),
         "tflops_at_median": round(w.flops() / (med * 1e-3) / 1e12, 3),
         "tflops_at_mean": round(w.flops() / (mean * 1e-3) / 1e12, 3),
@@ -295,7 +268,6 @@ def hbm_resident(torch, dev, stream, w, dA, dB, dC, launch, steps, min_warmup_ms
         "alg_hbm_gbs_at_median": round(gbs(med), 1),
         "hbm_frac_at_mean": round(gbs(mean) * 1e9 / measure.MI355X_HBM_BW, 4),
         "hbm_frac_at_median": round(gbs(med) * 1e9 / measure.MI355X_HBM_BW, 4),
-        "sclk_mhz": clock.report(),
     }
 
 
@@ -386,12 +358,11 @@ def main(argv=None) -> int:
     K = args.steps
     region0, region1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize(dev)
-    with ClockSampler() as clock:
-        region0.record(stream)
-        for _ in range(K):
-            step()
-        region1.record(stream)
-        torch.cuda.synchronize(dev)
+    region0.record(stream)
+    for _ in range(K):
+        step()
+    region1.record(stream)
+    torch.cuda.synchronize(dev)
 
     total_ms = region0.elapsed_time(region1)
 
@@ -448,6 +419,9 @@ def main(argv=None) -> int:
     roof_ms = hbm["mean_ms"] if hbm_figure else per_launch_ms
     achieved = flops / (roof_ms * 1e-3) / 1e12
     lib_path = pg.library_path()
+    vname = pg.VARIANT_NAMES.get(variant, str(variant))
+    if hbm is not None:
+        hbm["traffic"] = load_traffic(w.name, vname, "hbm_resident")
     out = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -468,16 +442,16 @@ def main(argv=None) -> int:
             "transA": w.trans_a, "transB": w.trans_b,
             "alpha": w.alpha, "beta": w.beta,
             "inputs": f"{'U(-1,1)' if w.dist == 'uniform' else 'N(0,1)'} fp32, seed {w.seed}",
-            "variant": pg.VARIANT_NAMES.get(variant, str(variant)),
+            "variant": vname,
             "device": props.name,
             "cus": props.multi_processor_count,
         },
         "pct_of_fp32_mfma_peak": round(100.0 * value * 1e9 / measure.MI355X_FP32_MFMA_PEAK, 2),
         "roofline": roofline_entry(w, roof, achieved, peak, roof_ms,
-                                   load_traffic(w.name, pg.VARIANT_NAMES.get(variant,
-                                                                              str(variant))),
+                                   load_traffic(w.name, vname,
+                                                "hbm_resident" if hbm_figure else "back_to_back"),
                                    hbm_figure),
-        "sclk_mhz": clock.report(),
+        "sclk_mhz": clock_report(w.name, vname),
         "hbm_resident": hbm,
         "determinism": {"rerun_identical_bits": identical},
         "cold": cold,

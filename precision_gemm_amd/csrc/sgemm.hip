@@ -554,7 +554,18 @@ sgemm_mfma_kernel(Params p)
         for (int j = 0; j < TN; ++j)
             acc[i][j] = f32x16{};
 
-    f32x4 ra[OpA::SLOTS], rb[OpB::SLOTS];
+    // LATE_STORE (one wave group): two register buffers for the staged
+    // loads, by step parity. Step s issues the loads of step s + 2 first and
+    // writes step s + 1's data (loaded one step earlier) to LDS halfway
+    // through its MFMAs, so a load has about one and a half steps to arrive
+    // instead of one: operands streamed from HBM rather than the Infinity
+    // Cache then arrive in time (4092^3 with operands not cached: 1.14 ms
+    // with the writes at the start of the step, 0.93 ms with them halfway;
+    // at the end of the step the warm case lost 1 %, as the writes then
+    // delay the barrier).
+    constexpr bool LATE_STORE = WAVES_K == 1 && !WIDE;
+    constexpr int NBUF = LATE_STORE ? 2 : 1;
+    f32x4 ra[NBUF][OpA::SLOTS], rb[NBUF][OpB::SLOTS];
     const int nsteps = (Kt + BK - 1) / BK;
 
     // Every K-step after the first is full, so only the prologue's first load
@@ -564,9 +575,11 @@ sgemm_mfma_kernel(Params p)
     // k-contiguous operands.)
     using Masked = std::true_type;
     using Full = std::false_type;
-    auto load = [&](auto tail) {
-        opa.template load_next<decltype(tail)::value>(tid, ra);
-        opb.template load_next<decltype(tail)::value>(tid, rb);
+    using B0 = std::integral_constant<int, 0>;
+    using B1 = std::integral_constant<int, NBUF - 1>;
+    auto load = [&](auto tail, auto buf) {
+        opa.template load_next<decltype(tail)::value>(tid, ra[decltype(buf)::value]);
+        opb.template load_next<decltype(tail)::value>(tid, rb[decltype(buf)::value]);
     };
 
     constexpr int NQ = BK / 8 / WAVES_K; // groups of 8 k per K-step, per wave
@@ -595,10 +608,10 @@ sgemm_mfma_kernel(Params p)
         }
     };
 
-    load(Masked{});
-    OpA::store(lds, tid, ra);
-    OpB::store(lds + OpA::STAGE, tid, rb);
-    load(Full{});
+    load(Masked{}, B0{});
+    OpA::store(lds, tid, ra[0]);
+    OpB::store(lds + OpA::STAGE, tid, rb[0]);
+    load(Full{}, B1{});
     __syncthreads();
 
     // Software pipeline over K-steps. Group 0 of a stage is read right after
@@ -622,25 +635,57 @@ sgemm_mfma_kernel(Params p)
         // writes and loads are of no use but harmless (their windows lie past
         // the last K-step; a lane reads either memory inside the operand's
         // buffer range or, beyond it, zeros).
-        OpA::store(nxt, tid, ra);
-        OpB::store(nxt + OpA::STAGE, tid, rb);
-        load(tail);
+        constexpr int NW = OpA::SLOTS + OpB::SLOTS;      // LDS writes
+        constexpr int NL = NW * OpA::EPS;                // global loads
+        constexpr int NM = 4 * TM * TN * NQ - LATE;      // MFMAs before the barrier
+        if constexpr (LATE_STORE) {
+            // Loads of step s + 2 into the buffer step s's data left, then the
+            // MFMAs, with step s + 1's data written to LDS halfway through them.
+            load(tail, std::integral_constant<int, PAR>{});
 #pragma unroll
-        for (int q = 1; q < NQ - 1; ++q)
-            mfma_group(fa[q], fb[q], 0, 4 * TM * TN);
-        mfma_group(fa[NQ - 1], fb[NQ - 1], 0, 4 * TM * TN - LATE);
-        // Order: this stage's remaining fragment reads, then MFMAs alternating
-        // with the next stage's LDS writes and the global loads.
-        __builtin_amdgcn_sched_group_barrier(0x100, 4 * (TM + TN) * (NQ - 1), 0);
+            for (int q = 1; q < NQ - 1; ++q)
+                mfma_group(fa[q], fb[q], 0, 4 * TM * TN);
+            mfma_group(fa[NQ - 1], fb[NQ - 1], 0, 4 * TM * TN - LATE);
+            OpA::store(nxt, tid, ra[1 - PAR]);
+            OpB::store(nxt + OpA::STAGE, tid, rb[1 - PAR]);
+            // Order: this stage's remaining fragment reads, MFMAs alternating
+            // with the global loads, MFMAs, MFMAs alternating with the writes,
+            // the rest of the MFMAs.
+            __builtin_amdgcn_sched_group_barrier(0x100, 4 * (TM + TN) * (NQ - 1), 0);
 #pragma unroll
-        for (int w = 0; w < OpA::SLOTS + OpB::SLOTS; ++w) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0); // MFMA
-            __builtin_amdgcn_sched_group_barrier(0x200, 1, 0); // LDS write
-        }
+            for (int w = 0; w < NL; ++w) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0); // MFMA
+                __builtin_amdgcn_sched_group_barrier(0x020, 1, 0); // global load
+            }
+            constexpr int MID = (NM - NL - NW) / 2 > 0 ? (NM - NL - NW) / 2 : 0;
+            if constexpr (MID > 0)
+                __builtin_amdgcn_sched_group_barrier(0x008, MID, 0);
 #pragma unroll
-        for (int w = 0; w < (OpA::SLOTS + OpB::SLOTS) * OpA::EPS; ++w) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0); // MFMA
-            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0); // global load
+            for (int w = 0; w < NW; ++w) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0); // MFMA
+                __builtin_amdgcn_sched_group_barrier(0x200, 1, 0); // LDS write
+            }
+        } else {
+            OpA::store(nxt, tid, ra[0]);
+            OpB::store(nxt + OpA::STAGE, tid, rb[0]);
+            load(tail, B0{});
+#pragma unroll
+            for (int q = 1; q < NQ - 1; ++q)
+                mfma_group(fa[q], fb[q], 0, 4 * TM * TN);
+            mfma_group(fa[NQ - 1], fb[NQ - 1], 0, 4 * TM * TN - LATE);
+            // Order: this stage's remaining fragment reads, then MFMAs
+            // alternating with the next stage's LDS writes and the global loads.
+            __builtin_amdgcn_sched_group_barrier(0x100, 4 * (TM + TN) * (NQ - 1), 0);
+#pragma unroll
+            for (int w = 0; w < NW; ++w) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0); // MFMA
+                __builtin_amdgcn_sched_group_barrier(0x200, 1, 0); // LDS write
+            }
+#pragma unroll
+            for (int w = 0; w < NL; ++w) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0); // MFMA
+                __builtin_amdgcn_sched_group_barrier(0x020, 1, 0); // global load
+            }
         }
         __builtin_amdgcn_sched_barrier(0);
         __syncthreads();
