@@ -18,7 +18,9 @@ times the same call on several copies of A, B and C, used in turn, more than
 1 GiB in all: every launch reads operands that the launches between its
 copy's previous use have pushed out of L2 and the 256 MB Infinity Cache, so
 they come from HBM, while launches keep running back to back and the clock
-stays up. It gives the per-launch median, min and mean; for a workload whose
+stays up. It gives the mean (one event pair around the launches) and the
+per-launch median and min (each launch between its own events, which adds a
+few µs to a short kernel); for a workload whose
 figure of merit is its HBM rate (the skinny product and matrix-vector
 products) the roofline entry is taken from this mode. The GPU clock
 while each mode's kernel ran is read from the committed counter pass
@@ -246,6 +248,18 @@ def hbm_resident(torch, dev, stream, w, dA, dB, dC, launch, steps, min_warmup_ms
         if i % 8 == 0:
             torch.cuda.synchronize(dev)
     torch.cuda.synchronize(dev)
+    # The mean: one event pair around `steps` launches (per-launch events
+    # would add their own gaps, several µs for a short kernel); then the same
+    # number of launches again, each between two events, for the median and
+    # the minimum (which for short kernels carry that gap).
+    r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    r0.record(stream)
+    for k in range(steps):
+        one(i + k)
+    r1.record(stream)
+    torch.cuda.synchronize(dev)
+    mean = r0.elapsed_time(r1) / steps
+    i += steps
     events = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     events[0].record(stream)
     for k in range(steps):
@@ -254,13 +268,13 @@ def hbm_resident(torch, dev, stream, w, dA, dB, dC, launch, steps, min_warmup_ms
     torch.cuda.synchronize(dev)
     ms = [events[k].elapsed_time(events[k + 1]) for k in range(steps)]
     srt = sorted(ms)
-    med, mean = srt[len(srt) // 2], sum(ms) / len(ms)
+    med = srt[len(srt) // 2]
     gbs = lambda t: w.algorithmic_bytes() / (t * 1e-3) / 1e9  # noqa: E731
     from precision_gemm_amd import measure
     del As, Bs, Cs
     return {
-        "copies": copies, "bytes_rotated": copies * per, "warmup_launches": i,
-        "launches": steps,
+        "copies": copies, "bytes_rotated": copies * per, "warmup_launches": i - steps,
+        "launches": steps, "timing": "mean over one event pair; median and min per launch",
         "mean_ms": round(mean, 5), "median_ms": round(med, 5), "min_ms": round(srt[0], 5),
         "tflops_at_median": round(w.flops() / (med * 1e-3) / 1e12, 3),
         "tflops_at_mean": round(w.flops() / (mean * 1e-3) / 1e12, 3),

@@ -554,7 +554,7 @@ sgemm_mfma_kernel(Params p)
         for (int j = 0; j < TN; ++j)
             acc[i][j] = f32x16{};
 
-    // LATE_STORE (one wave group): two register buffers for the staged
+    // LATE_STORE: two register buffers for the staged
     // loads, by step parity. Step s issues the loads of step s + 2 first and
     // writes step s + 1's data (loaded one step earlier) to LDS halfway
     // through its MFMAs, so a load has about one and a half steps to arrive
@@ -563,7 +563,7 @@ sgemm_mfma_kernel(Params p)
     // with the writes at the start of the step, 0.93 ms with them halfway;
     // at the end of the step the warm case lost 1 %, as the writes then
     // delay the barrier).
-    constexpr bool LATE_STORE = WAVES_K == 1 && !WIDE;
+    constexpr bool LATE_STORE = !WIDE;
     constexpr int NBUF = LATE_STORE ? 2 : 1;
     f32x4 ra[NBUF][OpA::SLOTS], rb[NBUF][OpB::SLOTS];
     const int nsteps = (Kt + BK - 1) / BK;

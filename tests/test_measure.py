@@ -86,3 +86,27 @@ def test_bench_roofline_bound_follows_the_ridge():
     assert e["achieved"] == pytest.approx(277_872_640 / 1e-4 / 1e9, rel=1e-4)
     assert e["mfma_frac_at_achieved"] == pytest.approx(tflops / 157.3, abs=1e-4)
     assert "skinny_16384x64x4096_nt" in bench.HBM_FIGURE
+
+
+def test_bench_counter_summary_is_tied_to_kernel_code_and_variant(tmp_path, monkeypatch):
+    """bench.py takes traffic and clock figures from the committed counter
+    summary only while it describes the current kernel code and the variant
+    the run launches, per timing mode."""
+    import json
+    import bench
+    sha = bench.kernel_source_hash()
+    data = {"sgemm_4092": {"kernel_sha": sha, "variant": "M128x128", "bytes_per_launch": 11,
+                           "sclk_mhz": 2400},
+            "sgemm_4092@hbm": {"kernel_sha": sha, "variant": "M128x128", "bytes_per_launch": 22,
+                               "sclk_mhz": 2390},
+            "sgemm_1024": {"kernel_sha": "stale", "variant": "S64x64_K2", "bytes_per_launch": 33}}
+    path = tmp_path / "traffic.json"
+    path.write_text(json.dumps(data))
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(path))
+    assert bench.load_traffic("sgemm_4092", "M128x128") == 11
+    assert bench.load_traffic("sgemm_4092", "M128x128", "hbm_resident") == 22
+    assert bench.load_traffic("sgemm_4092", "L256x128") is None
+    assert bench.load_traffic("sgemm_1024", "S64x64_K2") is None
+    clk = bench.clock_report("sgemm_4092", "M128x128")
+    assert (clk["back_to_back"], clk["hbm_resident"]) == (2400, 2390)
+    assert bench.clock_report("sgemm_1024", "S64x64_K2")["back_to_back"] is None
