@@ -24,7 +24,8 @@ few µs to a short kernel); for a workload whose
 figure of merit is its HBM rate (the skinny product and matrix-vector
 products) the roofline entry is taken from this mode. The GPU clock
 while each mode's kernel ran is read from the committed counter pass
-(``sclk_mhz``: GRBM_GUI_ACTIVE over the kernel duration), and the run records
+(``sclk_mhz``: GRBM_GUI_ACTIVE over the kernel duration, for kernels long
+enough that the cycles it counts around each dispatch do not dominate), and the run records
 the library file it loaded (path and hash) and the host CPU.
 
 Prints one JSON line. ``value`` is GFLOP/s (2*M*N*K per GEMM over the timed
@@ -124,15 +125,33 @@ def load_traffic(workload: str, variant: str, mode: str = "back_to_back"):
     return None if entry is None else entry.get("bytes_per_launch")
 
 
+# Shortest kernel whose GRBM_GUI_ACTIVE count gives its clock: the count also
+# covers a fixed 11-17 k cycles around each dispatch (every workload's count
+# exceeds 2.4 GHz x its duration by that much, whatever its length), which
+# moves the figure by under 3 % only from about 250 us on.
+MIN_CLOCK_NS = 250_000
+
+
 def clock_report(workload: str, variant: str) -> dict:
     """The GPU clock while the kernel ran, from the committed counter pass:
     GRBM_GUI_ACTIVE (busy cycles of the graphics block, summed over the eight
-    XCDs) / 8 over the kernel's duration, per timing mode."""
+    XCDs) / 8 over the counting run's kernel duration, per timing mode. For a
+    kernel shorter than MIN_CLOCK_NS the figure is dominated by the cycles
+    counted around the dispatch: ``sclk_mhz`` is then None and only the raw
+    quotient is given (``gui_active_mhz``)."""
     out = {"source": "GRBM_GUI_ACTIVE / 8 / kernel duration in the committed rocprofv3 "
-                     "counter pass (profiles/traffic.json)"}
+                     "counter pass (profiles/traffic.json); null below "
+                     f"{MIN_CLOCK_NS // 1000} us of kernel, where the ~11-17 k cycles the "
+                     "counter adds around each dispatch dominate"}
     for mode in ("back_to_back", "hbm_resident"):
         entry = counter_entry(workload, variant, mode)
-        out[mode] = None if entry is None else entry.get("sclk_mhz")
+        if entry is None or not entry.get("counter_dur_ns"):
+            out[mode] = None
+            continue
+        raw = entry["gui_cycles"] / entry["counter_dur_ns"] * 1e3
+        out[mode] = {"sclk_mhz": round(raw) if entry["counter_dur_ns"] >= MIN_CLOCK_NS else None,
+                     "gui_active_mhz": round(raw),
+                     "counter_kernel_us": round(entry["counter_dur_ns"] / 1e3, 2)}
     return out
 
 
@@ -465,7 +484,7 @@ def main(argv=None) -> int:
                                    load_traffic(w.name, vname,
                                                 "hbm_resident" if hbm_figure else "back_to_back"),
                                    hbm_figure),
-        "sclk_mhz": clock_report(w.name, vname),
+        "clock": clock_report(w.name, vname),
         "hbm_resident": hbm,
         "determinism": {"rerun_identical_bits": identical},
         "cold": cold,

@@ -96,10 +96,13 @@ def test_bench_counter_summary_is_tied_to_kernel_code_and_variant(tmp_path, monk
     import bench
     sha = bench.kernel_source_hash()
     data = {"sgemm_4092": {"kernel_sha": sha, "variant": "M128x128", "bytes_per_launch": 11,
-                           "sclk_mhz": 2400},
+                           "gui_cycles": 2_208_000, "counter_dur_ns": 920_000},
             "sgemm_4092@hbm": {"kernel_sha": sha, "variant": "M128x128", "bytes_per_launch": 22,
-                               "sclk_mhz": 2390},
-            "sgemm_1024": {"kernel_sha": "stale", "variant": "S64x64_K2", "bytes_per_launch": 33}}
+                               "gui_cycles": 2_198_100, "counter_dur_ns": 919_700},
+            "sgemm_1024": {"kernel_sha": "stale", "variant": "S64x64_K2", "bytes_per_launch": 33},
+            "skinny_16384x64x4096_nt": {"kernel_sha": sha, "variant": "T64x64",
+                                        "bytes_per_launch": 44, "gui_cycles": 178_300,
+                                        "counter_dur_ns": 68_950}}
     path = tmp_path / "traffic.json"
     path.write_text(json.dumps(data))
     monkeypatch.setattr(bench, "TRAFFIC_FILE", str(path))
@@ -108,5 +111,9 @@ def test_bench_counter_summary_is_tied_to_kernel_code_and_variant(tmp_path, monk
     assert bench.load_traffic("sgemm_4092", "L256x128") is None
     assert bench.load_traffic("sgemm_1024", "S64x64_K2") is None
     clk = bench.clock_report("sgemm_4092", "M128x128")
-    assert (clk["back_to_back"], clk["hbm_resident"]) == (2400, 2390)
+    assert clk["back_to_back"]["sclk_mhz"] == 2400 and clk["hbm_resident"]["sclk_mhz"] == 2390
     assert bench.clock_report("sgemm_1024", "S64x64_K2")["back_to_back"] is None
+    # a 69 us kernel: the raw quotient (2586 MHz, above the part's 2.4 GHz) is
+    # reported, but not as the clock
+    short = bench.clock_report("skinny_16384x64x4096_nt", "T64x64")["back_to_back"]
+    assert short["sclk_mhz"] is None and short["gui_active_mhz"] == 2586
