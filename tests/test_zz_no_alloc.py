@@ -4,7 +4,8 @@ through the C ABI, against the split-K entry point it mirrors
 workspace of the same size): the same bits on two calls in a row, the second
 smaller, so the second reuses the array the first left behind. Also checked
 against the oracle's bound, and a forced split too large for the array is
-refused before anything runs."""
+refused before anything runs. Captured into a HIP graph, its calls replay to
+the eager bits."""
 import sys
 
 import numpy as np
@@ -85,3 +86,62 @@ def test_noalloc_refuses_a_split_beyond_its_array(env):
     assert st == -23 and "scratch" in pg.sgemm_status_string(st)
     torch.cuda.synchronize(dev)
     assert int(torch.count_nonzero(C)) == 0
+
+
+def test_noalloc_in_a_captured_graph(env):
+    """The callers this entry point is for include code under HIP graph
+    capture: two calls (an automatic split of a deep-K product and a forced
+    split) captured into one graph replay to the eager bits, replay after
+    replay, with other eager work in between. The partial tiles of both calls
+    share the array, one call after the other on the captured stream."""
+    torch, pg = env
+    dev = torch.device("cuda:0")
+    rng = np.random.default_rng(91)
+    # (a forced split needs a tile kernel: these shapes get the K-split tile)
+    cases = [(0, 1, 256, 256, 16384, 2, 1.0, 2.0, 0), (1, 1, 1024, 768, 4000, 1, -0.5, 0.25, 4)]
+    bufs = []
+    for tA, tB, M, N, K, batch, alpha, beta, splits in cases:
+        lda, ldb = (M if tA else K), (K if tB else N)
+        dA = torch.from_numpy(rng.uniform(-1, 1, batch * M * K).astype(np.float32)).to(dev)
+        dB = torch.from_numpy(rng.uniform(-1, 1, batch * K * N).astype(np.float32)).to(dev)
+        dC0 = torch.from_numpy(rng.uniform(-1, 1, batch * M * N).astype(np.float32)).to(dev)
+        bufs.append(((tA, tB, M, N, K, alpha, lda, ldb, beta, batch, splits), dA, dB, dC0,
+                     dC0.clone()))
+
+    def call(args, dA, dB, dC):
+        tA, tB, M, N, K, alpha, lda, ldb, beta, batch, splits = args
+        st = pg.sgemm_strided_batched_noalloc(tA, tB, M, N, K, alpha, dA, lda, dB, ldb, beta,
+                                              dC, N, batch, M * K, K * N, M * N, splits,
+                                              check=False)
+        assert st == 0, (st, pg.sgemm_status_string(st))
+
+    # eager bits (this also looks up the array's address and the CU count)
+    for args, dA, dB, dC0, dC in bufs:
+        call(args, dA, dB, dC)
+    torch.cuda.synchronize(dev)
+    want = [dC.cpu().numpy().view(np.uint32).copy() for (_, _, _, _, dC) in bufs]
+
+    log("[noalloc] capture two calls")
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream(dev)
+    side.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            for args, dA, dB, dC0, dC in bufs:
+                call(args, dA, dB, dC)
+    torch.cuda.current_stream(dev).wait_stream(side)
+    torch.cuda.synchronize(dev)
+
+    for rep in range(4):
+        for args, dA, dB, dC0, dC in bufs:
+            dC.copy_(dC0)  # beta != 0: every replay starts from the same C
+        torch.cuda.synchronize(dev)
+        g.replay()
+        torch.cuda.synchronize(dev)
+        for k, (args, dA, dB, dC0, dC) in enumerate(bufs):
+            assert np.array_equal(dC.cpu().numpy().view(np.uint32), want[k]), (rep, args)
+        # unrelated eager work between replays, itself through the array
+        call((0, 0, 768, 768, 1500, 1.0, 1500, 768, 0.0, 1, 2),
+             torch.rand(768 * 1500, device=dev), torch.rand(1500 * 768, device=dev),
+             torch.empty(768 * 768, device=dev))
+        torch.cuda.synchronize(dev)
