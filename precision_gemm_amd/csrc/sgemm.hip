@@ -2043,14 +2043,24 @@ extern "C" int sgemm_select_variant(int transA, int transB, int M, int N, int K,
         return SGEMM_VARIANT_T64x32;
     if (tiles32 <= cus || (M <= 32 && K >= 512))
         return SGEMM_VARIANT_T32x64;
-    // One skinny dimension (<= 64) over a deep K whose long operand is too
-    // large to stay in the 256 MB Infinity Cache from one call to the next
-    // (over 128 MiB): the four-wave 64 x 64 streaming kernel, whose 4-deep
-    // per-wave rings keep the most bytes in flight while that operand streams
-    // from HBM. A smaller long operand stays cached, and the tiles below do
-    // better on it.
-    const long long long_bytes = 4LL * (M > N ? M : N) * K * batch;
-    if ((M <= 64 || N <= 64) && K >= 512 && tiles64 <= 2 * cus && long_bytes > (128LL << 20))
+    // One skinny dimension (<= 64) over a deep K, one 64 x 64 tile per CU at
+    // most, a long operand contiguous in k and too large to stay in the
+    // 256 MB Infinity Cache from one call to the next (over 128 MiB), and the
+    // short operand contiguous along its outputs: the four-wave 64 x 64
+    // streaming kernel, whose 4-deep per-wave rings stream that operand from
+    // HBM faster than the K-split tile does in this layout (16384 x 64 x 4096
+    // NN with operands from HBM: 78.5 against 83.9 µs; 16384 x 64 x 8192 NN:
+    // 149.6 against 167.7 µs; 64 x 16384 x 4096 TT: 77.6 against 80.2 µs).
+    // In the other layouts, with two tiles per CU, or with a long operand
+    // that stays cached, the K-split tile below is as fast or faster
+    // (16384 x 64 x 4096 NT: 78.1 against 79.3 µs; TT 74.0 against 76.6 µs;
+    // 32768 x 64 x 4096 NN: 148.3 against 152.3 µs).
+    const bool long_a = M > N;
+    const long long long_bytes = 4LL * (long_a ? M : N) * K * batch;
+    const bool long_kc = long_a ? transA == 0 : transB == 1;
+    const bool short_outer = long_a ? transB == 0 : transA == 1;
+    if ((M <= 64 || N <= 64) && K >= 512 && tiles64 <= cus && long_kc && short_outer &&
+        long_bytes > (128LL << 20))
         return SGEMM_VARIANT_T64x64;
     // Otherwise the tile whose busiest CU finishes first: a CU receives
     // ceil(tiles / CUs) tiles, each costing its area over the variant's

@@ -245,11 +245,18 @@ def test_select_variant(pg):
         assert sel(0, 0, *shape, 1, True, 256) == pg.VARIANT_S64x64, shape
     assert sel(0, 0, 4096, 4096, 520, 1, True, 256) == pg.VARIANT_M128x128
     # beyond one 32 x 64 tile per CU, a skinny dimension with a long operand
-    # over 128 MiB streams through the 64 x 64 kernel, whatever the
-    # transposes; one of at most 128 MiB stays with the tiles
-    for tA, tB in ((0, 1), (0, 0), (1, 1), (1, 0)):
-        assert sel(tA, tB, 16384, 64, 4096, 1, True, 256) == pg.VARIANT_T64x64
-    assert sel(0, 1, 64, 16384, 8192, 1, True, 256) == pg.VARIANT_T64x64
+    # over 128 MiB, contiguous in k, against a short operand contiguous along
+    # its outputs, with one 64 x 64 tile per CU at most, streams through the
+    # 64 x 64 kernel; the other layouts, two tiles per CU and a long operand
+    # of at most 128 MiB go to the K-split tile
+    assert sel(0, 0, 16384, 64, 4096, 1, True, 256) == pg.VARIANT_T64x64
+    assert sel(1, 1, 64, 16384, 8192, 1, True, 256) == pg.VARIANT_T64x64
+    for tA, tB in ((0, 1), (1, 1), (1, 0)):
+        assert sel(tA, tB, 16384, 64, 4096, 1, True, 256) == pg.VARIANT_S64x64_K2
+    for tA, tB in ((0, 1), (0, 0), (1, 0)):
+        assert sel(tA, tB, 64, 16384, 4096, 1, True, 256) == pg.VARIANT_S64x64_K2
+    assert sel(0, 0, 32768, 64, 4096, 1, True, 256) == pg.VARIANT_S64x64_K2
+    assert sel(0, 0, 16384, 64, 4096, 1, True, 128) == pg.VARIANT_S64x64_K2
     assert sel(0, 1, 16384, 64, 2048, 1, True, 256) == pg.VARIANT_S64x64_K2
     assert sel(0, 1, 64, 16384, 2048, 1, True, 256) == pg.VARIANT_S64x64_K2
     assert sel(0, 1, 16384, 64, 128, 1, True, 256) != pg.VARIANT_T64x64
@@ -364,7 +371,8 @@ def test_select_variant_is_always_a_kernel(pg, tA, tB, M, N, K, batch, vec4, cus
     """Any valid shape gets a variant in range; without 4-float loads it is the
     1-float variant; with them, the GEMV kernels exactly for N == 1 with B
     transposed or M == 1 with A not (the vector contiguous in k); the 64 x 64 streaming kernel only for
-    a dimension of at most 64; the 64 x 32 one for M > 32 with at most one tile per CU and
+    a dimension of at most 64, one 64 x 64 tile per CU at most and the long
+    operand contiguous in k against a short one that is not; the 64 x 32 one for M > 32 with at most one tile per CU and
     K >= 512, or N <= 32 with one tile per CU or K >= 512; otherwise the
     32 x 64 one exactly for grids of at most one tile per CU or M <= 32 with
     K >= 512."""
@@ -373,7 +381,8 @@ def test_select_variant_is_always_a_kernel(pg, tA, tB, M, N, K, batch, vec4, cus
     if not vec4:
         assert v == pg.VARIANT_S64x64_V1
     if v == pg.VARIANT_T64x64:
-        assert min(M, N) <= 64 and K >= 512
+        assert min(M, N) <= 64 and K >= 512 and -(-M // 64) * -(-N // 64) * batch <= cus
+        assert (tA, tB) == ((0, 0) if M > N else (1, 1))
     few6432 = -(-M // 64) * -(-N // 32) * batch <= cus
     t6432 = M > 32 and (few6432 or K >= 512 if N <= 32 else few6432 and K >= 512)
     t3264 = -(-M // 32) * -(-N // 64) * batch <= cus or (M <= 32 and K >= 512)
