@@ -1,14 +1,19 @@
 """Dispatch sweep: time every kernel variant on a grid of shapes and report how
 far the library's automatic choice is from the fastest one.
 
-    python -m precision_gemm_amd.tune [--shapes default|quick|wide|mid] [--json out.json]
+    python -m precision_gemm_amd.tune [--shapes default|quick|wide|mid] [--hbm] [--json out.json]
     python -m precision_gemm_amd.tune --splitk [--json out.json]
 
 For each shape every applicable variant is timed on the same device buffers,
 interleaved over several rounds (so clock drift hits all variants alike); a
-variant's time is the median of its rounds, each round the mean of
-back-to-back launches between two HIP events on the launch stream, preceded by
-an untimed window of the same variant.
+variant's time is the median of its rounds. A round replays a HIP graph that
+holds a run of back-to-back launches of the variant (so the host's per-call
+cost does not pace short kernels), between two HIP events, after an untimed
+replay of the same graph. With --hbm the launches of the run cycle through
+copies of A, B and C, at least four and at least 1.25 GiB in all, so each
+launch reads operands that the others have pushed out of L2 and the 256 MB
+Infinity Cache: the operands come from HBM, as in a real workload whose
+operands do not stay cached.
 The report lists the fastest variant, the one `sgemm_select_variant` picks and
 the regret (automatic time / fastest time - 1). The cost model in the host
 dispatcher is fitted to these tables.
@@ -90,6 +95,11 @@ MID_SHAPES = [
 ]
 
 
+# Bytes of operand copies the --hbm mode cycles through (five times the
+# Infinity Cache).
+ROTATE_BYTES = 5 << 28
+
+
 def time_variant(torch, pg, stream, call, launches: int) -> float:
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
@@ -100,7 +110,31 @@ def time_variant(torch, pg, stream, call, launches: int) -> float:
     return e0.elapsed_time(e1) / launches * 1e3  # microseconds
 
 
-def sweep(shapes, rounds: int = 3, target_ms: float = 20.0, out=sys.stdout):
+def graph_of(torch, dev, launch, n: int):
+    """A HIP graph holding launch(0), ..., launch(n - 1) on its capture stream
+    (launch takes the copy index and the stream handle)."""
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream(dev)
+    side.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            for i in range(n):
+                launch(i, side.cuda_stream)
+    torch.cuda.current_stream(dev).wait_stream(side)
+    torch.cuda.synchronize(dev)
+    return g
+
+
+def time_graph(torch, stream, g, launches: int) -> float:
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    g.replay()
+    e1.record(stream)
+    e1.synchronize()
+    return e0.elapsed_time(e1) / launches * 1e3  # microseconds
+
+
+def sweep(shapes, rounds: int = 3, target_ms: float = 20.0, hbm: bool = False, out=sys.stdout):
     import torch
 
     import precision_gemm_amd as pg
@@ -121,14 +155,18 @@ def sweep(shapes, rounds: int = 3, target_ms: float = 20.0, out=sys.stdout):
     results = []
     for tA, tB, M, N, K, batch, beta in shapes:
         beta_t = 1.0 if beta != 0.0 else 0.0
+        per = 4 * batch * (M * K + K * N + M * N)
+        # (at most 2048 copies: for the smallest problems that is still more
+        # than the Infinity Cache holds, and it bounds the graph's length)
+        copies = max(4, min(2048, -(-ROTATE_BYTES // per))) if hbm else 1
 
         def buf(rows, cols):
-            return torch.rand((batch, rows, cols), device=dev, generator=gen) * 2 - 1
+            return torch.rand((copies, batch, rows, cols), device=dev, generator=gen) * 2 - 1
         A = buf(K, M) if tA else buf(M, K)
         B = buf(N, K) if tB else buf(K, N)
         C = buf(M, N)
-        lda, ldb = A.shape[2], B.shape[2]
-        sa, sb, sc = A.stride(0), B.stride(0), C.stride(0)
+        lda, ldb = A.shape[3], B.shape[3]
+        sa, sb, sc = A.stride(1), B.stride(1), C.stride(1)
         # The library first describes a stride-1 vector operand as contiguous
         # in k; its choice, and whether the GEMV kernels take the call (N == 1
         # or M == 1 with the vector contiguous in k; a few vectors, 2 to 8,
@@ -148,33 +186,45 @@ def sweep(shapes, rounds: int = 3, target_ms: float = 20.0, out=sys.stdout):
                                  pg.VARIANT_P128x128, pg.VARIANT_P64x64)
                     and (v != pg.VARIANT_GEMV or gemv_ok)]
 
-        def caller(v):
-            return lambda: pg.sgemm_strided_batched_variant(
-                tA, tB, M, N, K, 1.0, A, lda, B, ldb, beta_t, C, N, batch, sa, sb, sc, v,
-                stream=stream.cuda_stream)
-        calls = {v: caller(v) for v in variants}
-        launches = {}
-        for v, call in calls.items():
+        def launcher(v):
+            def launch(i, stream_handle):
+                j = i % copies
+                st = pg.sgemm_strided_batched_variant(
+                    tA, tB, M, N, K, 1.0, A[j], lda, B[j], ldb, beta_t, C[j], N, batch, sa, sb,
+                    sc, v, stream=stream_handle, check=False)
+                if st != 0:
+                    raise pg.SgemmError(st, pg.sgemm_status_string(st))
+            return launch
+        launches, graphs = {}, {}
+        for v in variants:
+            launch = launcher(v)
+            one_call = (lambda lv=launch: lv(0, stream.cuda_stream))
             for _ in range(2):
-                call()
+                one_call()
             torch.cuda.synchronize(dev)
-            one = time_variant(torch, pg, stream, call, 3)
-            launches[v] = max(3, min(500, int(target_ms * 1e3 / max(one, 1.0))))
-        # Each timed window follows an untimed one of the same variant: the
+            one = time_variant(torch, pg, stream, one_call, 3)
+            n = max(3, min(500, int(target_ms * 1e3 / max(one, 1.0))))
+            if hbm:
+                n = max(n, 2 * copies)
+            launches[v] = n
+            graphs[v] = graph_of(torch, dev, launch, n)
+        # Each timed replay follows an untimed one of the same graph: the
         # clock settles differently after an under-filled grid (a large tile
         # on a small problem leaves most CUs idle) and needs a few ms to
         # return to the level the variant itself sustains.
         times = {v: [] for v in variants}
         for _ in range(rounds):
             for v in variants:
-                time_variant(torch, pg, stream, calls[v], max(2, launches[v] // 2))
-                times[v].append(time_variant(torch, pg, stream, calls[v], launches[v]))
+                time_graph(torch, stream, graphs[v], launches[v])
+                times[v].append(time_graph(torch, stream, graphs[v], launches[v]))
         med = {v: statistics.median(ts) for v, ts in times.items()}
         best = min(med, key=med.get)
         flops = 2.0 * M * N * K * batch
         row = {
             "shape": {"transA": tA, "transB": tB, "M": M, "N": N, "K": K, "batch": batch,
                       "beta": beta},
+            "mode": "hbm_resident" if hbm else "back_to_back",
+            "copies": copies,
             "us": {pg.VARIANT_NAMES[v]: round(t, 2) for v, t in med.items()},
             "best": pg.VARIANT_NAMES[best],
             "auto": pg.VARIANT_NAMES[auto],
@@ -187,6 +237,8 @@ def sweep(shapes, rounds: int = 3, target_ms: float = 20.0, out=sys.stdout):
               f"({row['auto_tflops']} TFLOP/s), regret {100 * row['regret']:.1f} %  | " +
               " ".join(f"{pg.VARIANT_NAMES[v]}={t:.1f}" for v, t in med.items()),
               file=out, flush=True)
+        del graphs, A, B, C
+        torch.cuda.empty_cache()
     return results
 
 
@@ -277,6 +329,8 @@ def main(argv=None) -> int:
     ap.add_argument("--splitk", action="store_true",
                     help="compare the plain and split-K automatic calls on deep-K shapes")
     ap.add_argument("--rounds", type=int, default=3)
+    ap.add_argument("--hbm", action="store_true",
+                    help="rotate operand copies so that every launch reads them from HBM")
     ap.add_argument("--json", default=None, help="write the table as JSON here")
     args = ap.parse_args(argv)
     if args.splitk:
@@ -287,7 +341,7 @@ def main(argv=None) -> int:
         return 0
     shapes = {"default": DEFAULT_SHAPES, "quick": QUICK_SHAPES, "wide": WIDE_SHAPES,
               "mid": MID_SHAPES}[args.shapes]
-    res = sweep(shapes, rounds=args.rounds)
+    res = sweep(shapes, rounds=args.rounds, hbm=args.hbm)
     regrets = [r["regret"] for r in res]
     print(f"shapes {len(res)}: mean regret {100 * statistics.mean(regrets):.2f} %, "
           f"max {100 * max(regrets):.2f} %", flush=True)
