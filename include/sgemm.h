@@ -110,7 +110,9 @@ enum sgemm_variant {
     SGEMM_VARIANT_S64x64 = 2,   /*  64 x  64 tile, 4 waves, 4-float loads */
     SGEMM_VARIANT_S64x64_V1 = 3,/*  64 x  64 tile, 4 waves, 1-float loads (any alignment) */
     SGEMM_VARIANT_T64x64 = 4,   /*  64 x  64 tile, 4 waves each on every 4th K-step,
-                                    direct-to-LDS streaming (few tiles, deep K) */
+                                    direct-to-LDS streaming (at most one tile per CU over a
+                                    deep K, chosen where a long operand over 128 MiB is
+                                    contiguous in k and the short one is not) */
     SGEMM_VARIANT_L256x256 = 5, /* 256 x 256 tile, 8 waves (two per SIMD in one workgroup) */
     SGEMM_VARIANT_S64x64_K2 = 6,/*  64 x  64 tile, 8 waves: two groups of 4 split each
                                     32-deep K-step, partial tiles added in LDS */
