@@ -149,6 +149,26 @@ def test_workload_parity(env, name):
         log(f"  {rep}")
 
 
+@pytest.mark.parametrize("tA,tB,M,N", [(0, 0, 16384, 64), (1, 1, 64, 16384)])
+def test_streaming_kernel_at_full_size(env, tA, tB, M, N):
+    """The skinny product in the layouts the automatic dispatch streams through
+    the 64 x 64 streaming kernel (the long operand, 268 MB, contiguous in k;
+    the short one contiguous along its outputs), fp32 with beta = 1, checked
+    on the first and last row bands against the bound."""
+    torch, pg = env
+    w = Workload("stream_full", tA, tB, M, N, 4096, 1.0, 1.0, seed=61)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    assert pg.sgemm_select_variant(tA, tB, M, N, 4096, 1, 1, cus) == pg.VARIANT_T64x64
+    A, B, C = workloads.make_inputs(w)
+    log(f"[parity] streaming kernel tA={tA} tB={tB} {M}x{N}x4096")
+    st, got = run_gpu(env, w, A, B, C)
+    assert st == 0
+    check_untouched(w, C, got)
+    for rows in ((0, 48), (M - 48, M)):
+        rep = check_against_oracle(w, A, B, C, got, rows=rows)
+        log(f"  rows {rows}: {rep}")
+
+
 def test_workload_4092_sampled_elements(env):
     """Random elements across the whole 4092^3 output, each recomputed alone."""
     w = workloads.HEADLINE
