@@ -70,20 +70,26 @@ def file_sha16(path: str) -> str:
 
 
 def host_info() -> dict:
-    model = None
+    """The host CPU as /proc/cpuinfo names it (its first processor), with the
+    family and model numbers (which identify the part where a virtual machine
+    shortens the name), and the cores this process may use."""
+    fields = {}
     try:
         with open("/proc/cpuinfo") as f:
             for line in f:
-                if line.startswith("model name"):
-                    model = line.split(":", 1)[1].strip()
-                    break
+                if not line.strip():
+                    break  # end of the first processor's block
+                key, _, val = line.partition(":")
+                fields.setdefault(key.strip(), val.strip())
     except OSError:
         pass
     try:
         cores = len(os.sched_getaffinity(0))
     except AttributeError:  # pragma: no cover
         cores = os.cpu_count()
-    return {"cpu_model": model, "cores_available": cores}
+    return {"cpu_model": fields.get("model name"), "cpu_family": fields.get("cpu family"),
+            "cpu_model_number": fields.get("model"), "cores_available": cores,
+            "cpus_online": os.cpu_count()}
 
 
 def kernel_source_hash() -> str:
