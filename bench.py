@@ -92,6 +92,16 @@ def host_info() -> dict:
             "cpus_online": os.cpu_count()}
 
 
+def rocm_version():
+    """The installed ROCm release (its version file), or None where there is none."""
+    root = os.environ.get("ROCM_PATH", "/opt/rocm")
+    try:
+        with open(os.path.join(root, ".info", "version")) as f:
+            return f.read().strip() or None
+    except OSError:
+        return None
+
+
 def kernel_source_hash() -> str:
     """Hash of the device code of the kernel source (everything before its host
     section), comments and whitespace dropped: editing a comment or the host
@@ -483,6 +493,7 @@ def main(argv=None) -> int:
             "inputs": f"{'U(-1,1)' if w.dist == 'uniform' else 'N(0,1)'} fp32, seed {w.seed}",
             "variant": vname,
             "device": props.name,
+            "arch": getattr(props, "gcnArchName", None),
             "cus": props.multi_processor_count,
         },
         "pct_of_fp32_mfma_peak": round(100.0 * value * 1e9 / measure.MI355X_FP32_MFMA_PEAK, 2),
@@ -494,7 +505,8 @@ def main(argv=None) -> int:
         "hbm_resident": hbm,
         "determinism": {"rerun_identical_bits": identical},
         "cold": cold,
-        "software": {"torch": torch.__version__, "hip": getattr(torch.version, "hip", None)},
+        "software": {"torch": torch.__version__, "hip": getattr(torch.version, "hip", None),
+                     "rocm": rocm_version()},
         "library": {"path": os.path.relpath(lib_path, ROOT), "sha256_16": file_sha16(lib_path)},
         "host": host_info(),
         "cpu_baseline": None,

@@ -117,3 +117,19 @@ def test_bench_counter_summary_is_tied_to_kernel_code_and_variant(tmp_path, monk
     # reported, but not as the clock
     short = bench.clock_report("skinny_16384x64x4096_nt", "T64x64")["back_to_back"]
     assert short["sclk_mhz"] is None and short["gui_active_mhz"] == 2586
+
+
+def test_bench_host_and_rocm_records(tmp_path, monkeypatch):
+    """The bench line names the host CPU (model, family and model numbers,
+    cores usable) and the installed ROCm release from its version file, or
+    None where there is no such file."""
+    import bench
+    h = bench.host_info()
+    assert set(h) >= {"cpu_model", "cpu_family", "cpu_model_number", "cores_available"}
+    assert h["cores_available"] >= 1
+    (tmp_path / ".info").mkdir()
+    (tmp_path / ".info" / "version").write_text("9.8.7-123\n")
+    monkeypatch.setenv("ROCM_PATH", str(tmp_path))
+    assert bench.rocm_version() == "9.8.7-123"
+    monkeypatch.setenv("ROCM_PATH", str(tmp_path / "absent"))
+    assert bench.rocm_version() is None
