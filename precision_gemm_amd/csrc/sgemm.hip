@@ -2067,9 +2067,13 @@ extern "C" int sgemm_select_variant(int transA, int transB, int M, int N, int K,
     // relative efficiency. The efficiencies are fitted to sweeps of every
     // variant over 76 shapes (precision_gemm_amd/tune.py): 128 x 128 tiles
     // 1.00; the K-split 64 x 64 tile 0.88, for K >= 768; plain 64 x 64 tiles
-    // 0.85, or 1.05 for K <= 512, where a tile's fixed costs (the first loads,
+    // 0.85, or 1.05 for K <= 128, where a tile's fixed costs (the first loads,
     // the C stores) outweigh its short K loop and the small tiles, more of
-    // them resident per CU, overlap those costs better; the streaming 64 x 32
+    // them resident per CU, overlap those costs better (8192^2 x 128: 185 µs
+    // against 193; 2048^2 x 64: 10.1 against 10.7), and 0.99 for 128 < K <=
+    // 512, where the 128 x 128 tile wins an equal share of work per CU
+    // (4096^2 x 256: 70.7 against 75.4 µs; 256^3 x 128 items: 37.4 against
+    // 38.8) and loses only where it would leave CUs idle; the streaming 64 x 32
     // tile 0.78, for K >= 2048 (any value from 0.75 to 0.80 picks the same
     // variants on the sweeps), whose small area fills the last round of tiles
     // better (1152^2 x 4096: 100 µs against 118 µs for the K-split tile). The
@@ -2081,7 +2085,7 @@ extern "C" int sgemm_select_variant(int transA, int transB, int M, int N, int K,
     struct Choice { int variant, bm, bn, eff_pct; long long min_k; };
     const Choice choices[] = {{SGEMM_VARIANT_M128x128, 128, 128, 100, 0},
                               {SGEMM_VARIANT_S64x64_K2, 64, 64, 88, 768},
-                              {SGEMM_VARIANT_S64x64, 64, 64, K <= 512 ? 105 : 85, 0},
+                              {SGEMM_VARIANT_S64x64, 64, 64, K <= 128 ? 105 : K <= 512 ? 99 : 85, 0},
                               {SGEMM_VARIANT_T64x32, 64, 32, 78, 2048}};
     int best = SGEMM_VARIANT_M128x128;
     double best_cost = -1.0;

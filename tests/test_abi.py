@@ -237,13 +237,17 @@ def test_select_variant(pg):
     assert sel(0, 0, 1024, 512, 1024, 1, True, 128) != pg.VARIANT_T32x64   # two per CU
     assert sel(0, 0, 512, 512, 128, 3, True, 256) != pg.VARIANT_T32x64     # 384 tiles
     assert sel(0, 0, 512, 512, 2048, 8, True, 256) == pg.VARIANT_S64x64_K2
-    # ... and the plain 64 x 64 tile below K = 768; for K <= 512 it also beats
-    # the 128 x 128 tile on full grids (per-tile fixed costs dominate)
+    # ... and the plain 64 x 64 tile below K = 768; for K <= 128 it also beats
+    # the 128 x 128 tile on full grids (per-tile fixed costs dominate), while
+    # for 128 < K <= 512 the 128 x 128 tile takes an equal share of work per
+    # CU and the plain tile only the grids it fills better
     assert sel(0, 0, 1024, 1024, 512, 1, True, 256) == pg.VARIANT_S64x64
     assert sel(0, 0, 128, 128, 128, 1, True, 2) == pg.VARIANT_S64x64
-    for shape in ((2048, 2048, 512), (4096, 4096, 256), (8192, 8192, 128), (2048, 2048, 64)):
+    for shape in ((8192, 8192, 128), (2048, 2048, 64)):
         assert sel(0, 0, *shape, 1, True, 256) == pg.VARIANT_S64x64, shape
-    assert sel(0, 0, 4096, 4096, 520, 1, True, 256) == pg.VARIANT_M128x128
+    for shape, batch in (((2048, 2048, 512), 1), ((4096, 4096, 256), 1), ((256, 256, 256), 128),
+                         ((4096, 4096, 520), 1)):
+        assert sel(0, 0, *shape, batch, True, 256) == pg.VARIANT_M128x128, shape
     # beyond one 32 x 64 tile per CU, a skinny dimension with a long operand
     # over 128 MiB, contiguous in k, against a short operand contiguous along
     # its outputs, with one 64 x 64 tile per CU at most, streams through the
@@ -264,8 +268,8 @@ def test_select_variant(pg):
     assert sel(0, 0, 2048, 2048, 2048, 1, True, 64) == pg.VARIANT_M128x128
     # a tile whose grid would exceed one launch is passed over: 2^24 tiles of
     # 64 x 64 (2^32 work-items), while 2^22 tiles of 128 x 128 still fit
-    assert sel(0, 0, 1 << 29, 128, 256, 1, True, 256) == pg.VARIANT_M128x128
-    assert sel(0, 0, 1 << 20, 128, 256, 1, True, 256) == pg.VARIANT_S64x64
+    assert sel(0, 0, 1 << 29, 128, 128, 1, True, 256) == pg.VARIANT_M128x128
+    assert sel(0, 0, 1 << 20, 128, 128, 1, True, 256) == pg.VARIANT_S64x64
     # no 4-float loads: the 1-float variant
     assert sel(0, 0, 4092, 4092, 4092, 1, False, 256) == pg.VARIANT_S64x64_V1
     assert sel(3, 0, 4, 4, 4, 1, True, 256) == -1
