@@ -1,4 +1,5 @@
-"""Seeded random calls through the C ABI, compared bit for bit with the oracle.
+"""Seeded random calls through the C ABI, compared with the oracle: bit for bit
+on integer inputs, within its error bound on U(-1, 1) inputs.
 
 Each call draws its shape from ragged and tile-sized dimensions (1 to 1000), a
 transpose pair, padded leading dimensions, batch strides with gaps (some of
@@ -121,3 +122,50 @@ def test_random_calls_bitwise(env):
     for v in variants:
         assert checked.get(f"plain v{v}", 0) >= 30, v
     assert sum(n for k, n in checked.items() if k.startswith("ws ")) >= 200
+
+
+def test_random_calls_float_bound(env):
+    """The same entry points on U(-1, 1) inputs with deeper K (up to 4096, so
+    that split-K takes many slices and the reduction changes the summation
+    order): every element within the oracle's error bound."""
+    torch, pg = env
+    ws = torch.empty(64 << 20, dtype=torch.uint8, device=torch.device("cuda:0"))
+    rng = np.random.default_rng(8765)
+    variants = [-1] + list(T.ALL_VARIANTS)
+    sizes = [1, 7, 33, 64, 100, 129, 256, 300, 513]
+    ks = [1, 17, 64, 520, 1000, 2048, 4096]
+    n_checked = 0
+    for i in range(300):
+        while True:
+            M, N = (int(rng.choice(sizes)) for _ in range(2))
+            K, batch = int(rng.choice(ks)), int(rng.choice([1, 1, 2, 3]))
+            if M * N * K * batch <= 1.2e8:
+                break
+        tA, tB = int(rng.integers(2)), int(rng.integers(2))
+        pad = int(rng.choice([0, 4, 1]))
+        alpha, beta = float(rng.uniform(-2, 2)), float(rng.choice([0.0, 1.0, -0.75]))
+        lda, ldb, ldc = (M if tA else K) + pad, (K if tB else N) + pad, N + pad
+        w = Workload(f"fcall{i}", tA, tB, M, N, K, alpha, beta, seed=50000 + i, batch=batch,
+                     lda=lda, ldb=ldb, ldc=ldc)
+        A, B, C = workloads.make_inputs(w)
+        pick, variant = rng.random(), int(rng.choice(variants))
+        if pick < 0.3:
+            splits = int(rng.choice([0, 2, 5, 16]))
+            allowed = (0, -18, -19, -21)
+            st, got = run_split(env, w, A, B, C, variant, splits, ws, noalloc=False)
+        elif pick < 0.4:
+            allowed = (0, -19, -23)
+            st, got = run_split(env, w, A, B, C, -1, int(rng.choice([0, 3])), None, noalloc=True)
+        else:
+            allowed = (0, -18)
+            st, got = T.run_gpu(env, w, A, B, C, variant=variant)
+        assert st in allowed, (w, st, pg.sgemm_status_string(st))
+        if (i + 1) % 50 == 0:
+            log(f"  {i + 1} calls")
+        if st != 0:
+            continue
+        T.check_against_oracle(w, A, B, C, got)
+        T.check_untouched(w, C, got)
+        n_checked += 1
+    log(f"  {n_checked} calls within the bound")
+    assert n_checked >= 100
