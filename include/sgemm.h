@@ -57,7 +57,9 @@
  *        returns -22 when one batch item has more output tiles than one
  *        kernel launch holds: more than 2^31 - 1 work-items along the tile
  *        axis (for the 64 x 64 tiles, M x N beyond about 2^34 to 2^35
- *        elements per item, a C of 64 GiB or more).
+ *        elements per item, a C of 64 GiB or more). The no-allocation
+ *        entry point returns -23 for a split beyond its fixed array, and
+ *        sgemm_set_dispatch_overrides -24 / -25 for an invalid table.
  *    >0  a hipError_t raised when querying the device or launching.
  * sgemm_status_string() turns any status into a message.
  *
@@ -158,10 +160,45 @@ enum sgemm_variant {
  * transA == 1 and lda == 1 as transA == 0, lda == K; for K > 1), which
  * names the same memory. The leading dimensions are not among the arguments:
  * a call with one of 2^21 or more runs SGEMM_VARIANT_W64x64 (or its 1-float
- * form) in place of any tile or streaming variant returned here.
+ * form) in place of any tile or streaming variant returned here. An installed
+ * dispatch override for the shape (sgemm_set_dispatch_overrides) comes first.
  */
 int sgemm_select_variant(int transA, int transB, int M, int N, int K, int batch,
                          int vec4_ok, int num_cus);
+
+/*
+ * Per-shape dispatch overrides: the table an offline tuning sweep produces.
+ * "From 1% to 94% of cuBLAS, one kernel at a time" times every configuration
+ * that survives its resource filters and finds the best one differs from GPU
+ * to GPU (its autotuning step, "What 'sensible' means"); "Triton Optimization
+ * Reference (cuTile -> Triton)", section 4 (autotune breadth, per-GPU
+ * configuration lists), asks for a tuned choice per backend and GPU. Each
+ * record names one call shape and the variant the automatic choice takes for
+ * exactly that shape, in place of the cost model's: `entries` holds `count`
+ * records of seven ints {transA, transB, M, N, K, batch, variant}, in host
+ * memory the library copies (the caller keeps ownership). The shape is the
+ * one sgemm_select_variant receives, after its vector normalization. Of two
+ * records for one shape the later wins. A call replaces the whole table;
+ * count 0 clears it.
+ *
+ * A record may name any tile or streaming variant (all but SGEMM_VARIANT_GEMV
+ * and the persistent variants, which run only some shapes). The automatic
+ * choice, sgemm_select_variant included, honours a record only where the
+ * call's alignment allows the variant's load width; leading dimensions of
+ * 2^21 or more still run the 64-bit-addressed tile.
+ *
+ * Returns 0; -24 if `entries` is NULL with count > 0 or a record is invalid (a
+ * transpose flag other than 0 or 1, a negative size, a variant that may not be
+ * named); -25 if count < 0 or count > SGEMM_MAX_DISPATCH_OVERRIDES. On error the
+ * installed table is unchanged. Thread-safe: a call running concurrently
+ * with a replacement sees the old table or the new one. The table is
+ * process-wide and serves every device.
+ */
+#define SGEMM_MAX_DISPATCH_OVERRIDES (1 << 20)
+int sgemm_set_dispatch_overrides(const int *entries, int count);
+
+/* Number of shapes in the installed override table (0: none). */
+int sgemm_dispatch_override_count(void);
 
 /*
  * sgemm_strided_batched with the kernel variant forced (testing and tuning):

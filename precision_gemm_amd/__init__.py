@@ -21,6 +21,8 @@ __all__ = [
     "sgemm_strided_batched_ws_variant", "sgemm_workspace_size", "sgemm_select_splits",
     "sgemm_status_string", "sgemm_select_variant", "sgemm_window_ranges",
     "sgemm_strided_batched_noalloc", "NOALLOC_SCRATCH_BYTES", "matmul",
+    "sgemm_set_dispatch_overrides", "sgemm_dispatch_override_count", "load_dispatch_overrides",
+    "MAX_DISPATCH_OVERRIDES",
     "library_path",
     "VARIANT_AUTO", "VARIANT_L256x128", "VARIANT_M128x128", "VARIANT_S64x64",
     "VARIANT_S64x64_V1", "VARIANT_T64x64", "VARIANT_L256x256", "VARIANT_S64x64_K2",
@@ -120,6 +122,10 @@ def _load():
                                                   ll, ll, i, p]
     lib.sgemm_window_ranges.restype = i
     lib.sgemm_window_ranges.argtypes = [ll, i, i, ctypes.POINTER(ctypes.c_uint)]
+    lib.sgemm_set_dispatch_overrides.restype = i
+    lib.sgemm_set_dispatch_overrides.argtypes = [ctypes.POINTER(ctypes.c_int), i]
+    lib.sgemm_dispatch_override_count.restype = i
+    lib.sgemm_dispatch_override_count.argtypes = []
     _lib = lib
     return lib
 
@@ -327,6 +333,40 @@ def sgemm_select_variant(transA, transB, M, N, K, batch, vec4_ok, num_cus) -> in
     """C ABI ``sgemm_select_variant`` (host-side dispatch decision)."""
     return _load().sgemm_select_variant(int(transA), int(transB), M, N, K, batch,
                                         int(bool(vec4_ok)), num_cus)
+
+
+MAX_DISPATCH_OVERRIDES = 1 << 20  # SGEMM_MAX_DISPATCH_OVERRIDES
+
+
+def sgemm_set_dispatch_overrides(records, check=True) -> int:
+    """C ABI ``sgemm_set_dispatch_overrides``: install per-shape overrides of
+    the automatic choice, replacing any installed table. `records` is an
+    iterable of (transA, transB, M, N, K, batch, variant), the variant a
+    number or a name of VARIANT_NAMES; an empty iterable clears the table."""
+    by_name = {n: v for v, n in VARIANT_NAMES.items()}
+    flat = []
+    for rec in records:
+        if len(rec) != 7:
+            raise ValueError(f"an override record has 7 fields, got {rec!r}")
+        variant = by_name[rec[6]] if isinstance(rec[6], str) else int(rec[6])
+        flat.extend([int(x) for x in rec[:6]] + [variant])
+    n = len(flat) // 7
+    arr = (ctypes.c_int * len(flat))(*flat) if flat else None
+    return _check(_load().sgemm_set_dispatch_overrides(arr, n), check)
+
+
+def sgemm_dispatch_override_count() -> int:
+    """C ABI ``sgemm_dispatch_override_count``."""
+    return _load().sgemm_dispatch_override_count()
+
+
+def load_dispatch_overrides(path, check=True) -> int:
+    """Install the overrides a tuning sweep wrote (``python -m
+    precision_gemm_amd.tune --write-overrides PATH``): a JSON list of records
+    as sgemm_set_dispatch_overrides takes them."""
+    import json
+    with open(path) as f:
+        return sgemm_set_dispatch_overrides(json.load(f), check=check)
 
 
 def sgemm_window_ranges(left_bytes, step_bytes, nsteps):

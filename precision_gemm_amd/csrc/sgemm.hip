@@ -53,7 +53,9 @@
 
 #include <atomic>
 #include <mutex>
+#include <shared_mutex>
 #include <type_traits>
+#include <unordered_map>
 #include <stdint.h>
 
 #include "sgemm.h"
@@ -1984,7 +1986,77 @@ int validate(int tA, int tB, int M, int N, int K, const float *A, int lda, const
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
+// Per-shape dispatch overrides: exact call shapes and the variant the
+// automatic choice takes for each, installed by the caller from an offline
+// sweep. Every automatic choice looks its shape up, so with no table
+// installed the lookup is one atomic load.
+struct ShapeKey {
+    int tA, tB, M, N, K, batch;
+    bool operator==(const ShapeKey &o) const
+    {
+        return tA == o.tA && tB == o.tB && M == o.M && N == o.N && K == o.K && batch == o.batch;
+    }
+};
+struct ShapeHash {
+    size_t operator()(const ShapeKey &k) const
+    {
+        uint64_t h = 0x9e3779b97f4a7c15ull;
+        for (const int v : {k.tA, k.tB, k.M, k.N, k.K, k.batch})
+            h = (h ^ (uint32_t)v) * 0x100000001b3ull;
+        return (size_t)h;
+    }
+};
+using OverrideTable = std::unordered_map<ShapeKey, int, ShapeHash>;
+std::shared_mutex g_override_mutex;
+OverrideTable g_overrides;
+std::atomic<int> g_override_count{0};
+
+// Variants an override may name: those that run any shape (the tiles, the
+// streaming tiles and the 64-bit-addressed tiles), not the matrix-vector or
+// persistent kernels, which take only some.
+bool overridable(int v)
+{
+    return v >= 0 && v < SGEMM_VARIANT_COUNT && v != SGEMM_VARIANT_GEMV && !is_persistent(v);
+}
+
+// The override for this shape, or -1.
+int override_for(int tA, int tB, int M, int N, int K, int batch)
+{
+    if (g_override_count.load(std::memory_order_acquire) == 0)
+        return -1;
+    std::shared_lock<std::shared_mutex> lock(g_override_mutex);
+    const auto it = g_overrides.find(ShapeKey{tA, tB, M, N, K, batch});
+    return it == g_overrides.end() ? -1 : it->second;
+}
+
 } // namespace
+
+extern "C" int sgemm_set_dispatch_overrides(const int *entries, int count)
+{
+    if (count < 0 || count > SGEMM_MAX_DISPATCH_OVERRIDES)
+        return -25;
+    if (count > 0 && entries == nullptr)
+        return -24;
+    OverrideTable table;
+    table.reserve((size_t)count);
+    for (int i = 0; i < count; ++i) {
+        const int *e = entries + 7 * i;
+        if ((e[0] != 0 && e[0] != 1) || (e[1] != 0 && e[1] != 1) || e[2] < 0 || e[3] < 0 ||
+            e[4] < 0 || e[5] < 0 || !overridable(e[6]))
+            return -24;
+        table[ShapeKey{e[0], e[1], e[2], e[3], e[4], e[5]}] = e[6]; // a later record wins
+    }
+    // (the previous table is freed after the lock is released)
+    std::unique_lock<std::shared_mutex> lock(g_override_mutex);
+    g_overrides.swap(table);
+    g_override_count.store((int)g_overrides.size(), std::memory_order_release);
+    return 0;
+}
+
+extern "C" int sgemm_dispatch_override_count(void)
+{
+    return g_override_count.load(std::memory_order_acquire);
+}
 
 extern "C" int sgemm_select_variant(int transA, int transB, int M, int N, int K, int batch,
                                     int vec4_ok, int num_cus)
@@ -1995,6 +2067,11 @@ extern "C" int sgemm_select_variant(int transA, int transB, int M, int N, int K,
     if (N < 0) return -4;
     if (K < 0) return -5;
     if (batch < 0) return -14;
+    // An installed override for exactly this shape, where the call's
+    // alignment allows its load width.
+    const int ov = override_for(transA, transB, M, N, K, batch);
+    if (ov >= 0 && (vec4_ok || kVariants[ov].vec == 1))
+        return ov;
     if (!vec4_ok)
         return SGEMM_VARIANT_S64x64_V1;
     // A matrix-vector product (N == 1, or M == 1 as its transpose) whose
@@ -2871,6 +2948,8 @@ extern "C" const char *sgemm_status_string(int status)
     case -21: return "workspace too small for the requested split count";
     case -22: return "problem too large: one batch item has more output tiles than one launch holds";
     case -23: return "split too large: its partial tiles exceed the fixed scratch of the no-allocation entry point (SGEMM_NOALLOC_SCRATCH_BYTES)";
+    case -24: return "invalid dispatch override: entries is NULL, or a record has a transpose flag other than 0 or 1, a negative size or a variant that may not be named";
+    case -25: return "invalid dispatch override count: negative or above SGEMM_MAX_DISPATCH_OVERRIDES";
     default: break;
     }
     if (status < 0)

@@ -2,6 +2,7 @@
 far the library's automatic choice is from the fastest one.
 
     python -m precision_gemm_amd.tune [--shapes default|quick|wide|mid] [--hbm] [--json out.json]
+                                      [--write-overrides overrides.json [--min-regret 0.02]]
     python -m precision_gemm_amd.tune --splitk [--json out.json]
 
 For each shape every applicable variant is timed on the same device buffers,
@@ -16,7 +17,9 @@ Infinity Cache: the operands come from HBM, as in a real workload whose
 operands do not stay cached.
 The report lists the fastest variant, the one `sgemm_select_variant` picks and
 the regret (automatic time / fastest time - 1). The cost model in the host
-dispatcher is fitted to these tables.
+dispatcher is fitted to these tables. --write-overrides turns the shapes it
+misses into a per-shape table for `sgemm_set_dispatch_overrides`, which the
+automatic choice then follows for exactly those shapes.
 
 Inputs are U(-1, 1) fp32 from a fixed seed. Only whether beta is zero changes
 the work (C is read iff beta != 0), so a nonzero beta is timed as 1.0, which
@@ -242,6 +245,31 @@ def sweep(shapes, rounds: int = 3, target_ms: float = 20.0, hbm: bool = False, o
     return results
 
 
+NOT_OVERRIDABLE = ("GEMV", "P128x128", "P64x64")  # variants that run only some shapes
+
+
+def overrides_from(rows, min_regret=0.02):
+    """Dispatch override records (sgemm_set_dispatch_overrides) from a sweep:
+    one per shape whose fastest variant beat the automatic choice by at least
+    `min_regret`, naming that variant. The shape is given as the automatic
+    choice receives it, a vector operand with adjacent k elements described
+    contiguous in k (the sweep's leading dimensions are the stored row
+    lengths, so an N == 1 op(B) untransposed and an M == 1 op(A) transposed
+    are such vectors)."""
+    records = []
+    for r in rows:
+        if r["best"] == r["auto"] or r["regret"] < min_regret or r["best"] in NOT_OVERRIDABLE:
+            continue
+        s = r["shape"]
+        tA, tB = s["transA"], s["transB"]
+        if s["N"] == 1 and tB == 0 and s["K"] > 1:
+            tB = 1
+        if s["M"] == 1 and tA == 1 and s["K"] > 1:
+            tA = 0
+        records.append([tA, tB, s["M"], s["N"], s["K"], s["batch"], r["best"]])
+    return records
+
+
 # Deep-K shapes with few output tiles, for the split-K comparison.
 SPLITK_SHAPES = [
     (0, 0, 256, 256, 4096, 1), (0, 0, 256, 256, 16384, 1), (0, 0, 128, 128, 65536, 1),
@@ -332,6 +360,11 @@ def main(argv=None) -> int:
     ap.add_argument("--hbm", action="store_true",
                     help="rotate operand copies so that every launch reads them from HBM")
     ap.add_argument("--json", default=None, help="write the table as JSON here")
+    ap.add_argument("--write-overrides", default=None, metavar="PATH",
+                    help="write dispatch overrides for the shapes the automatic choice "
+                         "misses (load them with precision_gemm_amd.load_dispatch_overrides)")
+    ap.add_argument("--min-regret", type=float, default=0.02,
+                    help="smallest regret that earns an override (default 0.02)")
     args = ap.parse_args(argv)
     if args.splitk:
         res = splitk_sweep(SPLITK_SHAPES, rounds=args.rounds)
@@ -348,6 +381,11 @@ def main(argv=None) -> int:
     if args.json:
         with open(args.json, "w") as f:
             json.dump(res, f, indent=1)
+    if args.write_overrides:
+        records = overrides_from(res, args.min_regret)
+        with open(args.write_overrides, "w") as f:
+            json.dump(records, f, indent=1)
+        print(f"{len(records)} dispatch overrides written to {args.write_overrides}", flush=True)
     return 0
 
 

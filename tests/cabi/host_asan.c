@@ -7,7 +7,10 @@
  * seeded arguments:
  *   - every status string;
  *   - the dispatch decisions (sgemm_select_variant, sgemm_select_splits) over
- *     random shapes, batches, CU counts and variants, checking their ranges;
+ *     random shapes, batches, CU counts and variants, checking their ranges,
+ *     with a per-shape override table installed;
+ *   - the override table itself (sgemm_set_dispatch_overrides): lookups,
+ *     refusal of invalid tables, random replacement and clearing;
  *   - the buffer-window countdown (sgemm_window_ranges) against the bytes
  *     left, for operands of up to 300 GiB;
  *   - argument validation of every entry point, and quick returns, with
@@ -91,6 +94,57 @@ static void dispatch(int rounds)
     /* invalid arguments of the chooser */
     CHECK(sgemm_select_variant(2, 0, 4, 4, 4, 1, 1, 256) < 0, "transA = 2 accepted");
     CHECK(sgemm_select_variant(0, 0, -1, 4, 4, 1, 1, 256) < 0, "M = -1 accepted");
+}
+
+/* Per-shape dispatch overrides: install, look up, refuse invalid tables
+   whole, replace and clear, with seeded random tables in between. */
+static void overrides(int rounds)
+{
+    enum { NREC = 64 };
+    int rec[7 * NREC];
+    for (int i = 0; i < NREC; ++i) {
+        int *e = rec + 7 * i;
+        e[0] = i & 1;
+        e[1] = (i >> 1) & 1;
+        e[2] = 64 + i;
+        e[3] = 128;
+        e[4] = 256;
+        e[5] = 1 + i % 3;
+        e[6] = i % 2 ? SGEMM_VARIANT_M128x128 : SGEMM_VARIANT_W64x64_V1;
+    }
+    CHECK(sgemm_set_dispatch_overrides(rec, NREC) == 0, "override table refused");
+    CHECK(sgemm_dispatch_override_count() == NREC, "override count");
+    for (int i = 0; i < NREC; ++i) {
+        const int *e = rec + 7 * i;
+        const int v = sgemm_select_variant(e[0], e[1], e[2], e[3], e[4], e[5], 1, 256);
+        CHECK(v == e[6], "override %d: %d, want %d", i, v, e[6]);
+    }
+    rec[7 * 10 + 6] = SGEMM_VARIANT_GEMV;
+    CHECK(sgemm_set_dispatch_overrides(rec, NREC) == -24, "GEMV override accepted");
+    CHECK(sgemm_dispatch_override_count() == NREC, "refused table changed the installed one");
+    CHECK(sgemm_set_dispatch_overrides(NULL, 1) == -24, "NULL entries accepted");
+    CHECK(sgemm_set_dispatch_overrides(NULL, -1) == -25, "negative count accepted");
+    int *big = (int *)malloc(7 * 4096 * sizeof(int));
+    for (int r = 0; r < rounds; ++r) {
+        const int n = (int)(next_u64() % 4096);
+        int valid = 1;
+        for (int i = 0; i < 7 * n; ++i) {
+            const int f = i % 7;
+            big[i] = f < 2 ? (int)(next_u64() % 2) : f < 6 ? (int)(next_u64() % 3000)
+                                                           : (int)(next_u64() % SGEMM_VARIANT_COUNT);
+            if (f == 6 && (big[i] == SGEMM_VARIANT_GEMV || big[i] >= SGEMM_VARIANT_P128x128))
+                valid = 0;
+        }
+        if (n > 0 && next_u64() % 8 == 0) {
+            big[7 * (n - 1) + 2] = -1; /* a negative size */
+            valid = 0;
+        }
+        const int st = sgemm_set_dispatch_overrides(n ? big : NULL, n);
+        CHECK(st == (valid ? 0 : -24), "random table %d: %d", r, st);
+    }
+    free(big);
+    CHECK(sgemm_set_dispatch_overrides(rec, 0) == 0, "clearing refused");
+    CHECK(sgemm_dispatch_override_count() == 0, "table not cleared");
 }
 
 static void windows(int rounds)
@@ -180,7 +234,14 @@ static void arguments(void)
 int main(void)
 {
     status_strings();
-    dispatch(200000);
+    overrides(300);
+    /* the chooser fuzz with a table installed, so every choice looks up */
+    {
+        int one[7] = {0, 0, 100, 100, 100, 1, SGEMM_VARIANT_S64x64};
+        CHECK(sgemm_set_dispatch_overrides(one, 1) == 0, "override table refused");
+        dispatch(200000);
+        CHECK(sgemm_set_dispatch_overrides(NULL, 0) == 0, "clearing refused");
+    }
     windows(2000);
     arguments();
     printf("host checks: %d failures\n", failures);
