@@ -82,6 +82,15 @@ def _load():
         raise ImportError(
             f"{path} is missing: the HIP library must be built first "
             "(python -c 'import __graft_entry__ as g; g.build()')")
+    # The library links the HIP runtime by its soname. Loaded after torch, it
+    # binds to the runtime torch already loaded, and both share one view of
+    # the devices. Loaded first, it brings in a second runtime next to
+    # torch's, and its device calls then fail. So torch, when installed, is
+    # imported first.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     lib = ctypes.CDLL(path)
     i, f, p, ll = ctypes.c_int, ctypes.c_float, ctypes.c_void_p, ctypes.c_longlong
     lib.sgemm.restype = i

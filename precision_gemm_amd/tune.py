@@ -3,6 +3,7 @@ far the library's automatic choice is from the fastest one.
 
     python -m precision_gemm_amd.tune [--shapes default|quick|wide|mid] [--hbm] [--json out.json]
                                       [--write-overrides overrides.json [--min-regret 0.02]]
+                                      [--load-overrides overrides.json]
     python -m precision_gemm_amd.tune --splitk [--json out.json]
 
 For each shape every applicable variant is timed on the same device buffers,
@@ -365,7 +366,14 @@ def main(argv=None) -> int:
                          "misses (load them with precision_gemm_amd.load_dispatch_overrides)")
     ap.add_argument("--min-regret", type=float, default=0.02,
                     help="smallest regret that earns an override (default 0.02)")
+    ap.add_argument("--load-overrides", default=None, metavar="PATH",
+                    help="install these dispatch overrides first, so that the automatic "
+                         "choice measured is the overridden one")
     args = ap.parse_args(argv)
+    if args.load_overrides:
+        import precision_gemm_amd as pg
+        pg.load_dispatch_overrides(args.load_overrides)
+        print(f"{pg.sgemm_dispatch_override_count()} dispatch overrides installed", flush=True)
     if args.splitk:
         res = splitk_sweep(SPLITK_SHAPES, rounds=args.rounds)
         if args.json:

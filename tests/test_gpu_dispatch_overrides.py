@@ -120,3 +120,26 @@ def test_misaligned_call_ignores_a_four_float_override(env):
     finally:
         pg.sgemm_set_dispatch_overrides([])
     assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+
+
+def test_library_loaded_before_torch(env):
+    """Installing overrides (or any call of the binding) before torch is
+    imported must not leave the process with a second HIP runtime: in a fresh
+    process, load the library first, then import torch and run a GEMM."""
+    import os
+    import subprocess
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    code = "\n".join([
+        "import precision_gemm_amd as pg",
+        "assert pg.sgemm_dispatch_override_count() == 0  # the library is loaded here",
+        "import torch",
+        "x = torch.ones(64 * 64, device='cuda')",
+        "y = torch.zeros(64 * 64, device='cuda')",
+        "pg.sgemm(0, 0, 64, 64, 64, 1.0, x, 64, x, 64, 0.0, y, 64)",
+        "torch.cuda.synchronize()",
+        "assert float(y[0]) == 64.0 and float(y[-1]) == 64.0",
+        "print('ok')",
+    ])
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=240,
+                       cwd=root)
+    assert r.returncode == 0 and "ok" in r.stdout, r.stderr[-2000:]
