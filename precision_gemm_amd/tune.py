@@ -2,7 +2,8 @@
 far the library's automatic choice is from the fastest one.
 
     python -m precision_gemm_amd.tune [--shapes default|quick|wide|mid] [--hbm] [--json out.json]
-                                      [--write-overrides overrides.json [--min-regret 0.02]]
+                                      [--write-overrides overrides.json [--min-regret 0.02]
+                                       [--both-modes]]
                                       [--load-overrides overrides.json]
     python -m precision_gemm_amd.tune --splitk [--json out.json]
 
@@ -249,14 +250,34 @@ def sweep(shapes, rounds: int = 3, target_ms: float = 20.0, hbm: bool = False, o
 NOT_OVERRIDABLE = ("GEMV", "P128x128", "P64x64")  # variants that run only some shapes
 
 
-def overrides_from(rows, min_regret=0.02):
+def overrides_from(rows, min_regret=0.02, other=None):
     """Dispatch override records (sgemm_set_dispatch_overrides) from a sweep:
     one per shape whose fastest variant beat the automatic choice by at least
     `min_regret`, naming that variant. The shape is given as the automatic
     choice receives it, a vector operand with adjacent k elements described
     contiguous in k (the sweep's leading dimensions are the stored row
     lengths, so an N == 1 op(B) untransposed and an M == 1 op(A) transposed
-    are such vectors)."""
+    are such vectors).
+
+    With `other`, the rows of the same shapes timed in the other mode, a
+    variant is judged by the sum of its two times: a table tuned with the
+    operands in cache then does not pick a variant that loses with them
+    streamed from HBM (1024^3: the plain 64 x 64 tile is 3 % faster than the
+    K-split tile back to back and 25 % slower HBM-resident)."""
+    if other is not None:
+        paired = {tuple(sorted(o["shape"].items())): o for o in other}
+        merged = []
+        for r in rows:
+            o = paired.get(tuple(sorted(r["shape"].items())))
+            if o is None or o["auto"] != r["auto"]:
+                continue
+            us = {v: t + o["us"][v] for v, t in r["us"].items() if v in o["us"]}
+            if r["auto"] not in us:
+                continue
+            best = min(us, key=us.get)
+            merged.append({"shape": r["shape"], "best": best, "auto": r["auto"],
+                           "regret": us[r["auto"]] / us[best] - 1.0})
+        rows = merged
     records = []
     for r in rows:
         if r["best"] == r["auto"] or r["regret"] < min_regret or r["best"] in NOT_OVERRIDABLE:
@@ -366,6 +387,9 @@ def main(argv=None) -> int:
                          "misses (load them with precision_gemm_amd.load_dispatch_overrides)")
     ap.add_argument("--min-regret", type=float, default=0.02,
                     help="smallest regret that earns an override (default 0.02)")
+    ap.add_argument("--both-modes", action="store_true",
+                    help="sweep back to back and HBM-resident, and judge each variant by "
+                         "the sum of its two times (for --write-overrides)")
     ap.add_argument("--load-overrides", default=None, metavar="PATH",
                     help="install these dispatch overrides first, so that the automatic "
                          "choice measured is the overridden one")
@@ -382,15 +406,19 @@ def main(argv=None) -> int:
         return 0
     shapes = {"default": DEFAULT_SHAPES, "quick": QUICK_SHAPES, "wide": WIDE_SHAPES,
               "mid": MID_SHAPES}[args.shapes]
-    res = sweep(shapes, rounds=args.rounds, hbm=args.hbm)
-    regrets = [r["regret"] for r in res]
-    print(f"shapes {len(res)}: mean regret {100 * statistics.mean(regrets):.2f} %, "
-          f"max {100 * max(regrets):.2f} %", flush=True)
+    runs = [sweep(shapes, rounds=args.rounds, hbm=hbm)
+            for hbm in ((False, True) if args.both_modes else (args.hbm,))]
+    for res in runs:
+        regrets = [r["regret"] for r in res]
+        print(f"shapes {len(res)} ({res[0]['mode'] if res else '-'}): mean regret "
+              f"{100 * statistics.mean(regrets):.2f} %, max {100 * max(regrets):.2f} %",
+              flush=True)
     if args.json:
         with open(args.json, "w") as f:
-            json.dump(res, f, indent=1)
+            json.dump([r for res in runs for r in res], f, indent=1)
     if args.write_overrides:
-        records = overrides_from(res, args.min_regret)
+        records = overrides_from(runs[0], args.min_regret,
+                                 other=runs[1] if len(runs) > 1 else None)
         with open(args.write_overrides, "w") as f:
             json.dump(records, f, indent=1)
         print(f"{len(records)} dispatch overrides written to {args.write_overrides}", flush=True)

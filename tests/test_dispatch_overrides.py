@@ -162,3 +162,23 @@ def test_sweep_rows_become_override_records(lib):
     assert sel(lib, 0, 1, 16384, 1, 4096) == lib.VARIANT_T64x32
     assert sel(lib, 0, 0, 1, 16384, 4096) == lib.VARIANT_T32x64
     assert tune.overrides_from(rows, min_regret=0.1) == []
+
+
+def test_override_records_judged_over_both_modes(lib):
+    """With the same shapes timed HBM-resident as well, a variant is judged by
+    the sum of its two times: a win back to back that is a loss from HBM
+    earns no record, a win in both does."""
+    from precision_gemm_amd import tune
+
+    def row(M, us, auto):
+        best = min(us, key=us.get)
+        return {"shape": {"transA": 0, "transB": 0, "M": M, "N": M, "K": M, "batch": 1,
+                          "beta": 0.0}, "us": us, "best": best, "auto": auto,
+                "regret": us[auto] / us[best] - 1.0}
+
+    b2b = [row(1024, {"S64x64": 19.2, "S64x64_K2": 19.7}, "S64x64_K2"),
+           row(1536, {"S64x64": 68.4, "S64x64_K2": 70.8}, "S64x64_K2")]
+    hbm = [row(1024, {"S64x64": 26.8, "S64x64_K2": 21.1}, "S64x64_K2"),
+           row(1536, {"S64x64": 69.0, "S64x64_K2": 71.0}, "S64x64_K2")]
+    assert [r[2] for r in tune.overrides_from(b2b, 0.02)] == [1024, 1536]
+    assert tune.overrides_from(b2b, 0.02, other=hbm) == [[0, 0, 1536, 1536, 1536, 1, "S64x64"]]
