@@ -177,7 +177,10 @@ int sgemm_select_variant(int transA, int transB, int M, int N, int K, int batch,
  * exactly that shape, in place of the cost model's: `entries` holds `count`
  * records of seven ints {transA, transB, M, N, K, batch, variant}, in host
  * memory the library copies (the caller keeps ownership). The shape is the
- * one sgemm_select_variant receives, after its vector normalization. Of two
+ * one sgemm_select_variant receives, after its vector normalization; a
+ * column-major call is looked up as the row-major product it runs, C^T =
+ * op(B)^T op(A)^T (M and N exchanged, transA = the call's transB and
+ * transB = its transA). Of two
  * records for one shape the later wins. A call replaces the whole table;
  * count 0 clears it.
  *
